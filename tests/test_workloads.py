@@ -1,0 +1,67 @@
+"""The workload table and the seeded input generator (CPU only)."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_attn_amd.workloads import BY_NAME, WORKLOADS, gen_qkv, slice_seed
+
+
+def _pairs_brute(w):
+    t = np.arange(w.seq_q, dtype=np.int64)
+    if not w.causal:
+        return w.seq_q * w.seq_kv
+    return int(np.minimum(w.q_pos0 + t + 1, w.seq_kv).clip(min=0).sum())
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
+def test_visible_pairs_closed_form_matches_count(w):
+    assert w.visible_pairs_per_head() == _pairs_brute(w)
+    assert w.seq_kv % w.num_chunks == 0
+    assert w.heads_q % w.heads_kv == 0
+    assert 0 <= w.rank < w.num_chunks
+    assert sorted(w.visit_order()) == list(range(w.num_chunks))
+    assert w.visit_order()[0] == w.rank
+
+
+def test_table_shapes():
+    shapes = [(w.dtype, w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_q, w.seq_kv,
+               w.num_chunks, w.rank, w.causal) for w in WORKLOADS]
+    assert shapes == [
+        ("f32", 1, 8, 2, 128, 1024, 1024, 4, 1, False),
+        ("bf16", 1, 32, 8, 128, 4096, 32768, 8, 3, True),
+        ("bf16", 16, 32, 32, 128, 4096, 16384, 4, 2, False),
+        ("bf16", 1, 64, 8, 128, 2048, 524288, 64, 32, True),
+        ("bf16", 16, 32, 8, 128, 1024, 131072, 16, 15, True),
+    ]
+    # Q shards sit at rank * Sq on the global axis for the causal workloads.
+    assert BY_NAME["llama3_8b_gqa_32k"].q_pos0 == 3 * 4096
+    assert BY_NAME["llama3_70b_gqa_512k"].q_pos0 == 262144
+    assert BY_NAME["gqa_b16_128k_heavy"].q_pos0 == 131072 - 1024
+    # Algorithmic flops of the headline workload (4 * D * B * Hq * pairs).
+    assert BY_NAME["llama3_8b_gqa_32k"].flops() == 4 * 128 * 32 * 58_722_304
+
+
+def test_generator_is_deterministic_and_slice_seeded():
+    kw = dict(batch=2, heads_q=4, heads_kv=2, seq_q=8, seq_kv=16, head_dim=8,
+              dtype=torch.bfloat16, seed=7)
+    a = gen_qkv(**kw)
+    b = gen_qkv(**kw)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # One slice can be regenerated alone from its seed.
+    g = torch.Generator().manual_seed(slice_seed(7, 1, 1, 0))
+    k10 = torch.randn((16, 8), generator=g).to(torch.bfloat16)
+    assert torch.equal(a[1][1, 0], k10)
+    assert a[0].dtype == torch.bfloat16 and a[0].shape == (2, 4, 8, 8)
+
+
+def test_heavy_rows():
+    q, k, v = gen_qkv(batch=1, heads_q=2, heads_kv=1, seq_q=4, seq_kv=1000, head_dim=16,
+                      dtype=torch.float32, seed=4, heavy_frac=0.01, heavy_mult=8.0)
+    g = torch.Generator().manual_seed(slice_seed(4, 1, 0, 0))
+    base = torch.randn((1000, 16), generator=g)
+    ratio = (k[0, 0] / base)
+    heavy = (ratio - 8.0).abs().amax(dim=1) < 1e-6
+    plain = (ratio - 1.0).abs().amax(dim=1) < 1e-6
+    assert int(heavy.sum()) == 10 and bool((heavy | plain).all())
