@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's shifted-chunk attention on one MI355X.
+
+A step is one fused ``attn_shifted_fwd`` launch over the 32K-context GQA rank
+shard (Llama-3-8B-like: batch 1, 32 query heads, 8 KV heads, head_dim 128, Q
+shard of 4096 rows at global offset 12288, KV of 32768 rows in 8 chunks
+visited in order (j + 3) % 8, causal), inputs resident in HBM.  Prints ONE
+JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Only one GPU is used: ``--gpus`` above 1 exits with a message.
+
+Extra modes (measurement plumbing, no effect on the default line):
+  --calib-copy-mib M   after the timed region, run one plain device copy of
+                       M MiB so a hardware-counter run sees a kernel of known
+                       traffic next to the attention kernel;
+  --summarize-pmc FETCH_CSV WRITE_CSV OUT
+                       turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE and
+                       WRITE_SIZE runs of this script with the copy) into the
+                       traffic summary read back by later runs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (AMD's "2.5 PFLOP/s" dense)
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["long_context_attention_attn_amd/csrc/attn_fwd.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_{workload}_traffic.json")
+METRIC = "attention TFLOP/s per MI355X + % bf16 MFMA peak, 32K-ctx GQA rank shard"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The fp64 oracle on the host, over whole (batch, head) slices of the
+    same workload until ``budget_s`` seconds have passed."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    group = w.heads_q // w.heads_kv
+    done_flops = 0
+    slices = 0
+    t_start = time.perf_counter()
+    elapsed = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads_q):
+            hk = h // group
+            rows = np.arange(w.seq_q)
+            qs, ks, vs = (q[b:b + 1, h:h + 1].cpu(), k[b:b + 1, hk:hk + 1].cpu(),
+                          v[b:b + 1, hk:hk + 1].cpu())
+            t0 = time.perf_counter()
+            oracle.attention_rows(qs, ks, vs, 0, 0, rows, causal=w.causal, q_pos0=w.q_pos0)
+            elapsed += time.perf_counter() - t0
+            done_flops += 4 * w.head_dim * w.visible_pairs_per_head()
+            slices += 1
+            if time.perf_counter() - t_start >= budget_s:
+                break
+        else:
+            continue
+        break
+    return {
+        "value": done_flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{slices} of {w.batch * w.heads_q} (batch, query-head) slices, every row, "
+                  f"fp64 numpy; {elapsed:.1f} s",
+    }
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out: str, workload: str, copy_mib: int):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention
+    kernel, scaled by what the same counters read for the calibration copy."""
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    def pick(vals, needle):
+        hits = [v for n, v in vals.items() if needle in n]
+        if not hits:
+            raise SystemExit(f"no kernel matching {needle!r} in counters")
+        flat = [x for v in hits for x in v]
+        return sum(flat) / len(flat)
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * 2**20
+    f_attn = pick(fetch, "attn_fwd_kernel") * 1024
+    w_attn = pick(write, "attn_fwd_kernel") * 1024
+    f_copy = pick(fetch, "copy") * 1024
+    w_copy = pick(write, "copy") * 1024
+    f_scale = copy_bytes / f_copy
+    w_scale = copy_bytes / w_copy
+    rec = {
+        "workload": workload,
+        "kernel_sha": kernel_hash(),
+        "fetch_bytes_raw": f_attn,
+        "write_bytes_raw": w_attn,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_raw": f_copy,
+        "copy_write_raw": w_copy,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "hbm_bytes_per_launch": f_attn * f_scale + w_attn * w_scale,
+    }
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_gqa_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0)
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, workload=args.workload,
+                      copy_mib=args.calib_copy_mib or 1024)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is not part of this library).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from long_context_attention_attn_amd import binding
+    from long_context_attention_attn_amd.workloads import BY_NAME, make_inputs
+
+    w = BY_NAME[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"bench: workload {w.name}: generating inputs")
+    q, k, v = make_inputs(w, dev)
+    out = torch.empty((w.batch, w.heads_q, w.seq_q, w.head_dim), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.batch, w.heads_q, w.seq_q), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        binding.attn_shifted_fwd(q, k, v, num_chunks=w.num_chunks, rank=w.rank,
+                                 causal=w.causal, q_pos0=w.q_pos0, out=out, lse=lse)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # The kernel runs on torch's current stream; events on that same stream
+    # bracket exactly the K launches.
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"bench: {ms:.4f} ms/step ({t_wall:.3f} s wall), {tflops:.1f} TFLOP/s")
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    is_f32 = w.dtype == "f32"
+    peak = PEAK_F32_TFLOPS if is_f32 else PEAK_BF16_TFLOPS
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if is_f32 else "bf16",
+        "data": "synthetic",
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": w.name,
+            "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+            "head_dim": w.head_dim, "seq_q": w.seq_q, "q_pos0": w.q_pos0,
+            "seq_kv": w.seq_kv, "num_chunks": w.num_chunks, "rank": w.rank,
+            "causal": w.causal, "algorithmic_gflop": round(flops / 1e9, 3),
+            "parallelism": "one rank's shard on 1 GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": read_traffic(w.name),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: cpu baseline (fp64 oracle, ~{args.cpu_seconds:.0f} s)")
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

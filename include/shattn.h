@@ -1,0 +1,143 @@
+/*
+ * shattn — shifted-chunk long-context attention for AMD MI355X (gfx950).
+ *
+ * One rank's share of ring/shifted long-context attention: a local query
+ * shard attends to a KV buffer split into J equal chunks that are visited in
+ * the rank-shifted order c_j = (j + i) % J, each chunk's partial output and
+ * log-sum-exp being merged online.  The shift order is the one CommIR's
+ * `shift` primitive introduces (papers.lqhl.me summary "Mercury (SOSP 2025)",
+ * section 核心方法 / core method); staggering the chunk order by rank is the
+ * temporal decoupling of the Silicon & Systems digest of Mercury, section
+ * "The hidden cost of synchronized operators".  The local attention itself
+ * is the kernel Mercury keeps as a "patch" (digest, section "CommIR makes
+ * communication transformable"); the pages do not write its arithmetic out,
+ * so the definitions below are the textbook ones.
+ *
+ * Common rules for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or retains user memory.
+ *  - Calls only enqueue work on `stream` (0 = the null stream) and never
+ *    synchronize; outputs are valid once the stream reaches that point.
+ *  - Every argument is validated on the host before anything is launched; on
+ *    failure the call returns a non-zero status and launches nothing.  No
+ *    exceptions cross this boundary and nothing aborts.
+ *  - NaN/Inf in inputs propagate to the outputs; they are never masked.
+ *  - Calls are stateless and thread-safe.
+ */
+#ifndef SHATTN_H
+#define SHATTN_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define SHATTN_API __attribute__((visibility("default")))
+#else
+#define SHATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SHATTN_OK = 0,
+  SHATTN_EINVAL = 1,       /* bad pointer, size, stride, alignment or rank  */
+  SHATTN_EUNSUPPORTED = 2, /* valid request this build does not implement   */
+  SHATTN_EHIP = 3          /* the HIP runtime reported an error at launch   */
+} shattn_status;
+
+typedef enum { SHATTN_BF16 = 0, SHATTN_F32 = 1 } shattn_dtype;
+
+/*
+ * Problem description shared by attn_chunk_fwd and attn_shifted_fwd.
+ *
+ * Q is [batch, heads_q, seq_q, head_dim]; K and V are
+ * [batch, heads_kv, seq_kv, head_dim]; O is [batch, heads_q, seq_q, head_dim].
+ * Strides are in ELEMENTS of the tensor's own dtype, for the (batch, head,
+ * sequence) axes; the head_dim axis must be contiguous (stride 1).
+ *
+ * Query head h reads KV head h / (heads_q / heads_kv) (contiguous GQA
+ * groups; heads_q == heads_kv is MHA).
+ *
+ * Query row t sits at global position q_pos0 + t.  With causal != 0, the key
+ * at global position p is visible to it iff p <= q_pos0 + t (inclusive).
+ * Scores are scale * (q . k); scale <= 0 selects 1/sqrt(head_dim).
+ * LSE values are natural logarithms of sum_k exp(score_k).
+ */
+typedef struct {
+  int32_t batch, heads_q, heads_kv, head_dim; /* head_dim must be 128       */
+  int64_t seq_q;                              /* Q-shard rows, >= 0         */
+  int64_t q_pos0;                             /* global position of Q row 0 */
+  int32_t causal;                             /* 0 or 1                     */
+  float scale;                                /* <= 0: 1/sqrt(head_dim)     */
+  int32_t in_dtype;                           /* shattn_dtype of Q, K, V    */
+  int32_t out_dtype;                          /* O dtype (attn_shifted_fwd) */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+} shattn_desc;
+
+/*
+ * attn_chunk_fwd — partial attention of the Q shard against ONE KV chunk.
+ *
+ * k, v point at the chunk's row 0 (global position kv_pos0); the chunk has
+ * kv_len rows (>= 0).  Writes the chunk's normalized partial output
+ * o_part (fp32, strided by desc->o_stride in fp32 elements) and its LSE
+ * lse_part (fp32, contiguous [batch, heads_q, seq_q]).  A row with no
+ * visible key in the chunk (kv_len == 0, or every key causally after it)
+ * gets O = 0 and LSE = -inf: the identity of lse_merge.
+ * desc->out_dtype is ignored (o_part is always fp32).
+ *
+ * Requirements: 16-byte aligned q, k, v, o_part; every (b, h, s) stride a
+ * multiple of 16 bytes; in_dtype BF16 or F32.
+ */
+SHATTN_API int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
+                   int64_t kv_len, int64_t kv_pos0, float* o_part, float* lse_part,
+                   hipStream_t stream);
+
+/*
+ * lse_merge — in place, row by row:
+ *   (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))
+ * with M = max(L_a, L_b), L = M + log(exp(L_a - M) + exp(L_b - M)),
+ * O = exp(L_a - L) O_a + exp(L_b - L) O_b.  Two empty rows (both LSE -inf)
+ * give O = 0, LSE = -inf; an empty side contributes nothing.  This is the
+ * exact decomposition of softmax over a disjoint union of key sets; the
+ * pages only say that each chunk's partial output and LSE are merged.
+ *
+ * o_acc/o_part are contiguous fp32 [rows, head_dim]; lse_acc/lse_part are
+ * contiguous fp32 [rows].  head_dim must be a multiple of 4 in [4, 256];
+ * all pointers 16-byte aligned (LSE pointers 4-byte).  The two sides must
+ * not alias.  rows == 0 is a valid no-op.
+ */
+SHATTN_API int lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc,
+              const float* o_part, const float* lse_part, hipStream_t stream);
+
+/*
+ * attn_shifted_fwd — rank `rank` of `num_chunks`, in ONE fused launch.
+ *
+ * k, v hold the whole KV buffer: row p is global position p, for
+ * p in [0, kv_len_total).  kv_len_total must be a multiple of num_chunks;
+ * chunk c covers [c*C, (c+1)*C) with C = kv_len_total / num_chunks.  Chunks
+ * are visited in the order c_j = (j + rank) % num_chunks, j = 0..J-1; chunks
+ * (or parts of chunks) that are causally invisible to a query tile are
+ * skipped; each visited chunk's softmax partial is merged into the running
+ * state with the same arithmetic as lse_merge.
+ *
+ * Writes O (desc->out_dtype: BF16 rounded to nearest even, or F32; strided by
+ * desc->o_stride) and LSE (fp32, contiguous [batch, heads_q, seq_q]).
+ * Rows with no visible key at all get O = 0, LSE = -inf.
+ *
+ * Requirements: as attn_chunk_fwd, plus 0 <= rank < num_chunks.
+ */
+SHATTN_API int attn_shifted_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
+                     int64_t kv_len_total, int32_t num_chunks, int32_t rank, void* o,
+                     float* lse, hipStream_t stream);
+
+/* attn_status_string — static, NUL-terminated name of a status code. */
+SHATTN_API const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHATTN_H */

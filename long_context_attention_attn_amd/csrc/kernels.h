@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace shattn {
+
+// Everything one forward launch needs.  Positions are global token positions.
+// Key row r of the K/V buffers sits at global position kv_pos0 + r.  The
+// buffer is walked as num_chunks chunks of chunk_len rows, chunk c covering
+// [kv_pos0 + c*chunk_len, kv_pos0 + (c+1)*chunk_len), visited in the order
+// (j + rank) % num_chunks.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_ss;  // element strides (batch, head, seq)
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t seq_q;
+  int64_t q_pos0;
+  int64_t kv_pos0;
+  int64_t chunk_len;
+  int32_t batch, heads_q, heads_kv, group;  // group = heads_q / heads_kv
+  int32_t num_chunks, rank;
+  int32_t causal;
+  float scale_log2;  // softmax scale times log2(e)
+  int32_t num_q_tiles;
+};
+
+enum class DType : int { BF16 = 0, F32 = 1 };
+
+// Query rows per workgroup of the forward kernels.
+constexpr int kBlockM = 128;
+
+// Launches the fused forward kernel on `stream`; returns the HIP launch status.
+hipError_t launch_attn_fwd(const FwdParams& p, DType in, DType out, hipStream_t stream);
+
+// Launches the row-wise (O, LSE) merge; rows > 0, head_dim % 4 == 0, <= 256.
+hipError_t launch_lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc,
+                            const float* o_part, const float* lse_part, hipStream_t stream);
+
+}  // namespace shattn

@@ -1,0 +1,74 @@
+// Row-wise merge of two partial attention results (O, LSE) over disjoint key
+// sets, in place into the accumulator pair:
+//   M = max(L_a, L_b), L = M + log(exp(L_a - M) + exp(L_b - M)),
+//   O = exp(L_a - L) O_a + exp(L_b - L) O_b,
+// with two empty rows (LSE -inf) staying empty.  This is how each chunk's
+// partial output and log-sum-exp are merged online in a shifted schedule
+// (papers.lqhl.me summary "Mercury (SOSP 2025)", section 核心方法; the pages
+// leave the arithmetic to the reader, this is the exact decomposition).
+//
+// HBM-bound elementwise work: every row is owned by exactly one wave and each
+// lane moves 16 bytes of O_a, O_b and the result, so the loads of lse_acc by
+// a row's lanes all precede the single store of that row's new LSE.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace shattn {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
+    int64_t rows, int32_t head_dim, int32_t rows_per_wave, float* __restrict__ o_acc,
+    float* __restrict__ lse_acc, const float* __restrict__ o_part,
+    const float* __restrict__ lse_part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kMergeThreads + threadIdx.x) >> 6;
+  const int pieces = head_dim >> 2;  // 16-byte pieces per row
+  const int r_local = lane / pieces;
+  const int c = lane - r_local * pieces;
+  const int64_t row = wave * rows_per_wave + r_local;
+  if (r_local >= rows_per_wave || row >= rows) return;
+
+  const float la = lse_acc[row];
+  const float lb = lse_part[row];
+  const float mx = fmaxf(la, lb);
+  const bool both_empty = (mx == -INFINITY);
+  const float ms = both_empty ? 0.f : mx;
+  const float wa = __expf(la - ms);
+  const float wb = __expf(lb - ms);
+  const float tot = wa + wb;
+  const float ca = both_empty ? 0.f : wa / tot;
+  const float cb = both_empty ? 0.f : wb / tot;
+  const float lse = both_empty ? -INFINITY : ms + __logf(tot);
+
+  const int64_t off = row * head_dim + c * 4;
+  f32x4 a = *(const f32x4*)(o_acc + off);
+  f32x4 bv = *(const f32x4*)(o_part + off);
+  *(f32x4*)(o_acc + off) = a * ca + bv * cb;
+  if (c == 0) lse_acc[row] = lse;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc,
+                            const float* o_part, const float* lse_part, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int32_t pieces = head_dim / 4;
+  const int32_t rows_per_wave = 64 / pieces;
+  const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+  const int64_t blocks = (waves * 64 + kMergeThreads - 1) / kMergeThreads;
+  int32_t hd = head_dim, rpw = rows_per_wave;
+  int64_t r = rows;
+  void* args[] = {&r, &hd, &rpw, &o_acc, &lse_acc, (void*)&o_part, (void*)&lse_part};
+  return hipLaunchKernel((const void*)&lse_merge_kernel, dim3((unsigned)blocks),
+                         dim3(kMergeThreads), args, 0, stream);
+}
+
+}  // namespace shattn

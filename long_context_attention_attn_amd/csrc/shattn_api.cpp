@@ -1,0 +1,176 @@
+// C-ABI entry points declared in include/shattn.h.
+//
+// Every argument is checked on the host before any HIP runtime call, so the
+// error paths need no GPU.  Each successful call enqueues exactly one kernel
+// on the caller's stream and returns the launch status; nothing synchronizes
+// and nothing is allocated.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/shattn.h"
+#include "kernels.h"
+
+namespace {
+
+using shattn::DType;
+using shattn::FwdParams;
+
+constexpr int32_t kSupportedHeadDim = 128;
+constexpr int64_t kPosLimit = (int64_t)1 << 60;  // keeps position arithmetic far from overflow
+
+bool valid_dtype(int32_t d) { return d == SHATTN_BF16 || d == SHATTN_F32; }
+
+int64_t elem_size(int32_t d) { return d == SHATTN_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A (batch, head, seq) stride triple: non-negative and a multiple of 16 bytes.
+bool strides_ok(const int64_t s[3], int64_t esize) {
+  for (int i = 0; i < 3; ++i) {
+    if (s[i] < 0 || s[i] > kPosLimit) return false;
+    if ((s[i] * esize) % 16 != 0) return false;
+  }
+  return true;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SHATTN_OK : SHATTN_EHIP; }
+
+// Checks shared by attn_chunk_fwd and attn_shifted_fwd.  `o_esize` is the
+// element size of the O tensor of the call.
+int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, int64_t kv_rows, int64_t o_esize) {
+  if (d == nullptr) return SHATTN_EINVAL;
+  if (d->batch < 0 || d->heads_q < 1 || d->heads_kv < 1) return SHATTN_EINVAL;
+  if (d->heads_q % d->heads_kv != 0) return SHATTN_EINVAL;
+  if (d->head_dim <= 0 || d->head_dim % 4 != 0) return SHATTN_EINVAL;
+  if (d->head_dim != kSupportedHeadDim) return SHATTN_EUNSUPPORTED;
+  if (d->seq_q < 0 || d->seq_q > kPosLimit) return SHATTN_EINVAL;
+  if (d->q_pos0 < 0 || d->q_pos0 > kPosLimit) return SHATTN_EINVAL;
+  if (d->causal != 0 && d->causal != 1) return SHATTN_EINVAL;
+  if (!isfinite(d->scale)) return SHATTN_EINVAL;
+  if (!valid_dtype(d->in_dtype)) return SHATTN_EINVAL;
+  const int64_t es = elem_size(d->in_dtype);
+  if (!strides_ok(d->q_stride, es) || !strides_ok(d->k_stride, es) ||
+      !strides_ok(d->v_stride, es) || !strides_ok(d->o_stride, o_esize))
+    return SHATTN_EINVAL;
+  const bool q_empty = d->batch == 0 || d->seq_q == 0;
+  const bool kv_empty = d->batch == 0 || kv_rows == 0;
+  if (!q_empty && (q == nullptr || o == nullptr || lse == nullptr)) return SHATTN_EINVAL;
+  if (!kv_empty && (k == nullptr || v == nullptr)) return SHATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SHATTN_EINVAL;
+  if (((uintptr_t)lse & 3u) != 0) return SHATTN_EINVAL;
+  // Grid size: one workgroup per 128 query rows of each (batch, head).
+  const int64_t tiles = (d->seq_q + shattn::kBlockM - 1) / shattn::kBlockM;
+  if (tiles * (int64_t)d->batch * d->heads_q > INT32_MAX) return SHATTN_EUNSUPPORTED;
+  return SHATTN_OK;
+}
+
+FwdParams make_params(const shattn_desc* d, const void* q, const void* k, const void* v,
+                      void* o, float* lse) {
+  FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_sb = d->q_stride[0];
+  p.q_sh = d->q_stride[1];
+  p.q_ss = d->q_stride[2];
+  p.k_sb = d->k_stride[0];
+  p.k_sh = d->k_stride[1];
+  p.k_ss = d->k_stride[2];
+  p.v_sb = d->v_stride[0];
+  p.v_sh = d->v_stride[1];
+  p.v_ss = d->v_stride[2];
+  p.o_sb = d->o_stride[0];
+  p.o_sh = d->o_stride[1];
+  p.o_ss = d->o_stride[2];
+  p.seq_q = d->seq_q;
+  p.q_pos0 = d->q_pos0;
+  p.batch = d->batch;
+  p.heads_q = d->heads_q;
+  p.heads_kv = d->heads_kv;
+  p.group = d->heads_q / d->heads_kv;
+  p.causal = d->causal;
+  const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634074);
+  p.num_q_tiles = (int32_t)((d->seq_q + shattn::kBlockM - 1) / shattn::kBlockM);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
+                   int64_t kv_len, int64_t kv_pos0, float* o_part, float* lse_part,
+                   hipStream_t stream) {
+  if (kv_len < 0 || kv_len > kPosLimit || kv_pos0 < 0 || kv_pos0 > kPosLimit)
+    return SHATTN_EINVAL;
+  int st = check_desc(desc, q, k, v, o_part, lse_part, kv_len, 4);
+  if (st != SHATTN_OK) return st;
+  FwdParams p = make_params(desc, q, k, v, o_part, lse_part);
+  p.kv_pos0 = kv_pos0;
+  p.chunk_len = kv_len;
+  p.num_chunks = 1;
+  p.rank = 0;
+  if (desc->batch == 0 || desc->seq_q == 0) return SHATTN_OK;
+  return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, DType::F32, stream));
+}
+
+int lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc, const float* o_part,
+              const float* lse_part, hipStream_t stream) {
+  if (rows < 0 || rows > kPosLimit) return SHATTN_EINVAL;
+  if (head_dim < 4 || head_dim > 256 || head_dim % 4 != 0) return SHATTN_EINVAL;
+  if (rows == 0) return SHATTN_OK;
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return SHATTN_EINVAL;
+  if (!aligned16(o_acc) || !aligned16(o_part)) return SHATTN_EINVAL;
+  if ((((uintptr_t)lse_acc) & 3u) || (((uintptr_t)lse_part) & 3u)) return SHATTN_EINVAL;
+  // The accumulator must not overlap the partial it reads.
+  const uintptr_t oa = (uintptr_t)o_acc, ob = (uintptr_t)o_part;
+  const uintptr_t la = (uintptr_t)lse_acc, lb = (uintptr_t)lse_part;
+  const uintptr_t obytes = (uintptr_t)rows * (uintptr_t)head_dim * 4u;
+  const uintptr_t lbytes = (uintptr_t)rows * 4u;
+  if (oa < ob + obytes && ob < oa + obytes) return SHATTN_EINVAL;
+  if (la < lb + lbytes && lb < la + lbytes) return SHATTN_EINVAL;
+  if (oa < la + lbytes && la < oa + obytes) return SHATTN_EINVAL;
+  return status_of(
+      shattn::launch_lse_merge(rows, head_dim, o_acc, lse_acc, o_part, lse_part, stream));
+}
+
+int attn_shifted_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
+                     int64_t kv_len_total, int32_t num_chunks, int32_t rank, void* o, float* lse,
+                     hipStream_t stream) {
+  if (num_chunks < 1 || rank < 0 || rank >= num_chunks) return SHATTN_EINVAL;
+  if (kv_len_total < 0 || kv_len_total > kPosLimit || kv_len_total % num_chunks != 0)
+    return SHATTN_EINVAL;
+  if (desc == nullptr || !valid_dtype(desc->out_dtype)) return SHATTN_EINVAL;
+  int st = check_desc(desc, q, k, v, o, lse, kv_len_total, elem_size(desc->out_dtype));
+  if (st != SHATTN_OK) return st;
+  FwdParams p = make_params(desc, q, k, v, o, lse);
+  p.kv_pos0 = 0;
+  p.chunk_len = kv_len_total / num_chunks;
+  p.num_chunks = num_chunks;
+  p.rank = rank;
+  if (desc->batch == 0 || desc->seq_q == 0) return SHATTN_OK;
+  return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, (DType)desc->out_dtype,
+                                           stream));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case SHATTN_OK:
+      return "SHATTN_OK";
+    case SHATTN_EINVAL:
+      return "SHATTN_EINVAL";
+    case SHATTN_EUNSUPPORTED:
+      return "SHATTN_EUNSUPPORTED";
+    case SHATTN_EHIP:
+      return "SHATTN_EHIP";
+    default:
+      return "SHATTN_UNKNOWN";
+  }
+}
+
+}  // extern "C"

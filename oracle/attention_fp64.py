@@ -190,9 +190,14 @@ def attention_rows(q, k, v, b: int, h: int, rows, *, causal: bool = False,
     rows = np.asarray(rows, dtype=np.int64)
     dim = q.shape[3]
     q_rows = _f64(q[b, h])[rows]
-    k64 = _f64(k[b, h // group])
-    v64 = _f64(v[b, h // group])
-    k_pos = kv_pos0 + np.arange(k64.shape[0], dtype=np.int64)
+    n_keys = k.shape[2]
+    if causal and len(rows):
+        # Keys after the last sampled query are invisible to every sampled row;
+        # leaving them out changes nothing and saves the fp64 upcast.
+        n_keys = int(min(n_keys, max(0, q_pos0 + rows.max() - kv_pos0 + 1)))
+    k64 = _f64(k[b, h // group][:n_keys])
+    v64 = _f64(v[b, h // group][:n_keys])
+    k_pos = kv_pos0 + np.arange(n_keys, dtype=np.int64)
     return attend_rows(q_rows, k64, v64, q_pos0 + rows, k_pos, causal=causal,
                        scale=_default_scale(dim, scale))
 

@@ -1,0 +1,159 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects every malformed call on the host before any HIP call.
+
+No case here reaches a kernel launch: each one breaks at least one rule the
+host checks, so it runs the same with or without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "shattn.h")
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def _lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libshattn.so not built")
+    return binding.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^SHATTN_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared_functions()
+    assert set(names) == {"attn_chunk_fwd", "lse_merge", "attn_shifted_fwd",
+                          "attn_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    _lib()
+    assert binding.attn_status_string(0) == "SHATTN_OK"
+    assert binding.attn_status_string(1) == "SHATTN_EINVAL"
+    assert binding.attn_status_string(2) == "SHATTN_EUNSUPPORTED"
+    assert binding.attn_status_string(3) == "SHATTN_EHIP"
+    assert binding.attn_status_string(77) == "SHATTN_UNKNOWN"
+
+
+def test_desc_layout_matches_header():
+    # int32 x4, int64 x2, int32, float, int32 x2, 4 x int64[3]
+    assert ctypes.sizeof(binding.ShattnDesc) == 16 + 16 + 16 + 4 * 24
+    assert binding.ShattnDesc.q_stride.offset == 48
+
+
+def _desc(**over):
+    d = binding.ShattnDesc()
+    d.batch, d.heads_q, d.heads_kv, d.head_dim = 1, 4, 2, 128
+    d.seq_q, d.q_pos0, d.causal, d.scale = 256, 0, 1, 0.0
+    d.in_dtype, d.out_dtype = binding.BF16, binding.BF16
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        setattr(d, name, (ctypes.c_int64 * 3)(4 * 256 * 128, 256 * 128, 128))
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def _shifted(lib, d, q=FAKE, k=FAKE, v=FAKE, total=1024, nch=4, rank=1, o=FAKE, lse=FAKE):
+    return lib.attn_shifted_fwd(ctypes.byref(d) if d is not None else None, q, k, v, total, nch,
+                                rank, o, lse, None)
+
+
+def _chunk(lib, d, q=FAKE, k=FAKE, v=FAKE, kv_len=256, kv_pos0=0, o=FAKE, lse=FAKE):
+    return lib.attn_chunk_fwd(ctypes.byref(d) if d is not None else None, q, k, v, kv_len,
+                              kv_pos0, o, lse, None)
+
+
+S3 = ctypes.c_int64 * 3
+
+
+@pytest.mark.parametrize("case,expect", [
+    ({"heads_q": 3}, 1),                # heads_q % heads_kv != 0
+    ({"heads_kv": 0}, 1),
+    ({"heads_q": 0}, 1),
+    ({"batch": -1}, 1),
+    ({"head_dim": 64}, 2),              # valid shape, not built
+    ({"head_dim": 130}, 1),             # not a multiple of 4
+    ({"seq_q": -5}, 1),
+    ({"q_pos0": -1}, 1),
+    ({"causal": 2}, 1),
+    ({"scale": float("nan")}, 1),
+    ({"scale": float("inf")}, 1),
+    ({"in_dtype": 7}, 1),
+    ({"out_dtype": 9}, 1),
+    ({"q_stride": S3(1, 1, 129)}, 1),   # row stride not a multiple of 16 bytes
+    ({"k_stride": S3(-128, 128, 128)}, 1),
+    ({"o_stride": S3(4, 4, 4)}, 1),
+])
+def test_shifted_rejects_bad_desc(case, expect):
+    lib = _lib()
+    assert _shifted(lib, _desc(**case)) == expect
+
+
+def test_shifted_rejects_bad_arguments():
+    lib = _lib()
+    d = _desc()
+    assert _shifted(lib, None) == 1
+    assert _shifted(lib, d, rank=4) == 1          # rank >= num_chunks
+    assert _shifted(lib, d, rank=-1) == 1
+    assert _shifted(lib, d, nch=0) == 1
+    assert _shifted(lib, d, total=1000, nch=3) == 1  # not a multiple
+    assert _shifted(lib, d, total=-4) == 1
+    assert _shifted(lib, d, q=0) == 1             # null pointers
+    assert _shifted(lib, d, k=0) == 1
+    assert _shifted(lib, d, v=0) == 1
+    assert _shifted(lib, d, o=0) == 1
+    assert _shifted(lib, d, lse=0) == 1
+    assert _shifted(lib, d, q=FAKE + 8) == 1      # misaligned
+    assert _shifted(lib, d, o=FAKE + 4) == 1
+    assert _shifted(lib, d, lse=FAKE + 2) == 1
+
+
+def test_chunk_rejects_bad_arguments():
+    lib = _lib()
+    d = _desc()
+    assert _chunk(lib, None) == 1
+    assert _chunk(lib, d, kv_len=-1) == 1
+    assert _chunk(lib, d, kv_pos0=-3) == 1
+    assert _chunk(lib, d, k=0) == 1
+    assert _chunk(lib, d, v=FAKE + 2) == 1
+    assert _chunk(lib, _desc(head_dim=256)) == 2
+    # o_part is fp32: a row stride of 6 floats (24 bytes) is not 16-byte aligned.
+    assert _chunk(lib, _desc(o_stride=S3(6, 6, 6)), kv_len=256) == 1
+
+
+def test_merge_rejects_bad_arguments():
+    lib = _lib()
+    a, b = 0x100000, 0x200000
+    la, lb = 0x300000, 0x400000
+    assert lib.lse_merge(-1, 128, a, la, b, lb, None) == 1
+    assert lib.lse_merge(10, 130, a, la, b, lb, None) == 1
+    assert lib.lse_merge(10, 0, a, la, b, lb, None) == 1
+    assert lib.lse_merge(10, 512, a, la, b, lb, None) == 1
+    assert lib.lse_merge(10, 128, 0, la, b, lb, None) == 1
+    assert lib.lse_merge(10, 128, a + 4, la, b, lb, None) == 1
+    assert lib.lse_merge(10, 128, a, la + 1, b, lb, None) == 1
+    assert lib.lse_merge(10, 128, a, la, a + 16, lb, None) == 1  # O sides overlap
+    assert lib.lse_merge(10, 128, a, la, b, la, None) == 1       # LSE sides alias
+    assert lib.lse_merge(10, 128, a, a + 64, b, lb, None) == 1   # LSE inside O
+    assert lib.lse_merge(0, 128, 0, 0, 0, 0, None) == 0          # empty: a no-op
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.attn_shifted_fwd(q, q, q, num_chunks=1, rank=0)
