@@ -115,7 +115,14 @@ def attend_rows(q_rows, k_rows, v_rows, q_pos, k_pos, *, causal: bool, scale: fl
         m_safe = np.where(empty, 0.0, m_row)
         p = np.exp(s - m_safe[:, None])  # masked entries give exp(-inf) = 0
         l_row = p.sum(axis=1)
-        o_blk = p @ vb
+        if np.isfinite(vb).all():
+            o_blk = p @ vb
+        else:
+            # Sum over each row's visible keys only, so that a non-finite
+            # value row reaches exactly the queries that see it (a masked
+            # weight of 0 times NaN would otherwise leak it).
+            o_blk = np.stack([p[i, p_vis] @ vb[p_vis] for i, p_vis in
+                              enumerate(np.isfinite(s))]) if len(s) else p @ vb
         with np.errstate(invalid="ignore", divide="ignore"):
             o_blk = np.where(empty[:, None], 0.0, o_blk / l_row[:, None])
             lse_blk = np.where(empty, -np.inf, m_safe + np.log(l_row))

@@ -281,3 +281,12 @@ def test_scalar_loop_tiny():
                     ref = sum(wi * v[0, 0, j, x] for wi, j in zip(w, keys)) / tot
                     assert abs(o[0, h, t, x] - ref) <= 1e-12
                 assert abs(lse[0, h, t] - (mx + math.log(tot))) <= 1e-12
+
+
+def test_nonfinite_value_reaches_only_rows_that_see_it():
+    q, k, v = _rand((1, 1, 8, 4), 95), _rand((1, 1, 8, 4), 96), _rand((1, 1, 8, 4), 97)
+    v[0, 0, 5, 2] = np.nan
+    o, lse = oracle.attention(q, k, v, causal=True, q_pos0=0)
+    assert np.isfinite(o[0, 0, :5]).all()
+    assert np.isnan(o[0, 0, 5:, 2]).all() and np.isfinite(np.delete(o[0, 0, 5:], 2, axis=1)).all()
+    assert np.isfinite(lse).all()
