@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (AMD's "2.5 PFLOP/s" dense)
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["long_context_attention_attn_amd/csrc/attn_fwd.hip"]
+KERNEL_SOURCES = ["long_context_attention_attn_amd/csrc/attn_fwd_bf16.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_{workload}_traffic.json")
 METRIC = "attention TFLOP/s per MI355X + % bf16 MFMA peak, 32K-ctx GQA rank shard"
 

@@ -60,6 +60,7 @@ struct Pick<false, A, B> {
 constexpr int kHeadDim = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kBlockM = kBlockMF32;
 static_assert(kBlockM == kWaves * 32, "one wave per 32 query rows");
 
 // Tile geometry per input type.
@@ -479,12 +480,14 @@ hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const FwdParams& p, DType in, DType out, hipStream_t stream) {
-  if (in == DType::BF16)
-    return out == DType::BF16 ? launch_typed<__bf16, __bf16>(p, stream)
-                              : launch_typed<__bf16, float>(p, stream);
+hipError_t launch_attn_fwd_f32(const FwdParams& p, DType out, hipStream_t stream) {
   return out == DType::BF16 ? launch_typed<float, __bf16>(p, stream)
                             : launch_typed<float, float>(p, stream);
+}
+
+hipError_t launch_attn_fwd(const FwdParams& p, DType in, DType out, hipStream_t stream) {
+  return in == DType::BF16 ? launch_attn_fwd_bf16(p, out, stream)
+                           : launch_attn_fwd_f32(p, out, stream);
 }
 
 }  // namespace shattn

@@ -35,11 +35,16 @@ struct FwdParams {
 
 enum class DType : int { BF16 = 0, F32 = 1 };
 
-// Query rows per workgroup of the forward kernels.
-constexpr int kBlockM = 128;
+// Query rows per workgroup of the forward kernels, per input type.
+constexpr int kBlockMBf16 = 256;
+constexpr int kBlockMF32 = 128;
+inline int block_m(DType in) { return in == DType::BF16 ? kBlockMBf16 : kBlockMF32; }
 
 // Launches the fused forward kernel on `stream`; returns the HIP launch status.
+// p.num_q_tiles must equal ceil(seq_q / block_m(in)).
 hipError_t launch_attn_fwd(const FwdParams& p, DType in, DType out, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const FwdParams& p, DType out, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const FwdParams& p, DType out, hipStream_t stream);
 
 // Launches the row-wise (O, LSE) merge; rows > 0, head_dim % 4 == 0, <= 256.
 hipError_t launch_lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc,

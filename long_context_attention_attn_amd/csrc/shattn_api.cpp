@@ -60,8 +60,9 @@ int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v
   if (!kv_empty && (k == nullptr || v == nullptr)) return SHATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SHATTN_EINVAL;
   if (((uintptr_t)lse & 3u) != 0) return SHATTN_EINVAL;
-  // Grid size: one workgroup per 128 query rows of each (batch, head).
-  const int64_t tiles = (d->seq_q + shattn::kBlockM - 1) / shattn::kBlockM;
+  // Grid size: one workgroup per block_m query rows of each (batch, head).
+  const int64_t bm = shattn::block_m((DType)d->in_dtype);
+  const int64_t tiles = (d->seq_q + bm - 1) / bm;
   if (tiles * (int64_t)d->batch * d->heads_q > INT32_MAX) return SHATTN_EUNSUPPORTED;
   return SHATTN_OK;
 }
@@ -95,7 +96,8 @@ FwdParams make_params(const shattn_desc* d, const void* q, const void* k, const 
   p.causal = d->causal;
   const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634074);
-  p.num_q_tiles = (int32_t)((d->seq_q + shattn::kBlockM - 1) / shattn::kBlockM);
+  const int64_t bm = shattn::block_m((DType)d->in_dtype);
+  p.num_q_tiles = (int32_t)((d->seq_q + bm - 1) / bm);
   return p;
 }
 
