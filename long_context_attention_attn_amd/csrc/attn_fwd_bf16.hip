@@ -3,17 +3,17 @@
 // A workgroup owns 256 query rows of one (batch, query head): eight waves of
 // 32 rows, two per SIMD.  It walks the KV chunks in the rank-shifted order
 // c_j = (j + rank) % J (the `shift` primitive of CommIR, papers.lqhl.me
-// summary "Mercury (SOSP 2025)", section 核心方法), 32 keys per tile, and
+// summary "Mercury (SOSP 2025)", section 核心方法), 64 keys per tile, and
 // carries the online-softmax state in registers across chunk boundaries.
 // Rescaling that state when a chunk starts is exactly the log-sum-exp merge
 // of the chunk's partial result, so one launch computes what attn_chunk_fwd
 // followed by lse_merge computes chunk by chunk.  Chunk ranges that no query
 // of the workgroup can see (causal) are skipped without touching memory.
 //
-// Matrix cores (v_mfma_f32_32x32x16_bf16), per wave and 32-key tile:
-//   S^T[key][q] = sum_d K[key][d] Q[q][d]          8 steps
+// Matrix cores (v_mfma_f32_32x32x16_bf16), per wave and 64-key tile:
+//   S^T[key][q] = sum_d K[key][d] Q[q][d]          2 key blocks x 8 steps
 //     A = K rows from LDS (ds_read_b128), B = Q^T resident in VGPRs.
-//   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]   4 d blocks x 2 steps
+//   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]   4 d blocks x 4 steps
 //     A = V^T, read from row-major V in LDS with the transposing
 //         ds_read_b64_tr_b16, B = P^T taken straight from the S^T accumulator.
 // Each lane owns one query column of S^T, so the softmax row max/sum are
@@ -58,12 +58,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kBlockMBf16;  // 256 query rows per workgroup
-constexpr int kN = 32;                // keys per tile
+constexpr int kN = 64;                // keys per tile
 constexpr int kKStride = 136;         // K row stride in LDS, elements (272 B)
 constexpr int kVStride = 144;         // V row stride in LDS, elements (288 B)
 constexpr int kKTile = kN * kKStride;
 constexpr int kVTile = kN * kVStride;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kChunks = kN * 16 / 256;  // 16-byte pieces per thread of a wave group
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 static_assert(kBlockM == kWaves * 32, "32 query rows per wave");
 
 struct TileWalk {
@@ -104,109 +105,127 @@ __device__ __forceinline__ bool walk_next(const FwdParams& p, int64_t limit, Til
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One 32-row x 256 B tile of K or V is 512 sixteen-byte pieces; the 256
-// threads of a wave group move two each.  Rows at or past t_end are read
-// from row t0 instead (always in bounds) and zeroed when stored, so neither
-// the loads nor the stores branch, and nothing waits for the loads until the
-// store a phase or two later.
+// A 64-row x 256 B tile of K or V is 1024 sixteen-byte pieces; the 256
+// threads of a wave group move kChunks each, piece id = gtid + 256*i (row
+// id/16, column piece id%16).  Rows at or past the tile end are read from the
+// tile's first row instead (always in bounds) and zeroed when stored, so
+// neither loads nor stores branch, and nothing waits for the loads until the
+// store two phases later.
 struct Stage {
-  u32x4 x[2];
-  bool ok[2];
+  u32x4 x[kChunks];
+  uint32_t ok;  // bit i: piece i lies inside the tile
 };
 
-__device__ __forceinline__ void gload_tile(const __bf16* base, int64_t row_stride, int64_t t0,
-                                           int64_t t_end, int64_t kv_pos0, int id0, Stage& st) {
+struct TileLoader {
+  int64_t off[kChunks];  // element offset of each piece from the tile's first row
+  int64_t off0[kChunks]; // the same piece column in the tile's first row
+  int row[kChunks];
+};
+
+__device__ __forceinline__ void loader_init(TileLoader& ld, int64_t row_stride, int gtid) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int id = id0 + 256 * i;
-    const int row = id >> 4, ch = id & 15;
-    st.ok[i] = t0 + row < t_end;
-    const int64_t key = st.ok[i] ? t0 + row : t0;
-    st.x[i] = *(const u32x4*)(base + (key - kv_pos0) * row_stride + ch * 8);
+  for (int i = 0; i < kChunks; ++i) {
+    const int id = gtid + 256 * i;
+    ld.row[i] = id >> 4;
+    ld.off0[i] = (id & 15) * 8;
+    ld.off[i] = (int64_t)ld.row[i] * row_stride + ld.off0[i];
   }
+}
+
+__device__ __forceinline__ void gload_tile(const __bf16* tile, int rows, const TileLoader& ld,
+                                           Stage& st) {
+  uint32_t ok = 0;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const bool in = ld.row[i] < rows;
+    ok |= (uint32_t)in << i;
+    st.x[i] = *(const u32x4*)(tile + (in ? ld.off[i] : ld.off0[i]));
+  }
+  st.ok = ok;
 }
 
 template <int kStride>
-__device__ __forceinline__ void lstore_tile(__bf16* dst, int id0, const Stage& st) {
+__device__ __forceinline__ void lstore_tile(__bf16* dst, int gtid, const Stage& st) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int id = id0 + 256 * i;
-    const int row = id >> 4, ch = id & 15;
+  for (int i = 0; i < kChunks; ++i) {
+    const int id = gtid + 256 * i;
+    const bool in = (st.ok >> i) & 1u;
     u32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = st.ok[i] ? st.x[i][e] : 0u;
-    *(u32x4*)(dst + row * kStride + ch * 8) = v;
+    for (int e = 0; e < 4; ++e) v[e] = in ? st.x[i][e] : 0u;
+    *(u32x4*)(dst + (id >> 4) * kStride + (id & 15) * 8) = v;
   }
 }
 
-// One MFMA phase: S^T of the wave's 32 queries against K tile `ks`, and
-// O^T += V^T P^T for V tile `vs` (vs_lane is this lane's source address for
-// the transposing read: row 4*(lane/32) + (lane/4)%4 of a 16-key step,
-// column 16*((lane/16)%2) + 4*(lane%4) of a 32-wide d block).  All LDS
-// operand reads are issued ahead of the matrix-core ops that consume them.
-__device__ __forceinline__ f32x16 mfma_phase(const __bf16* ks, const __bf16* vs_lane,
-                                             const bf16x8 (&qv)[8], const bf16x8 (&pb)[2],
-                                             f32x16 (&o)[4], int lq, int hh) {
-  const __bf16* krow = ks + lq * kKStride + hh * 8;
-  bf16x8 a[8], va[2][4];
-  auto read_v = [&](int ks2, int db) {
-    const __bf16* src = vs_lane + (ks2 * 16) * kVStride + db * 32;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * kVStride));
-    va[ks2][db].lo = __builtin_bit_cast(bf16x4, lo);
-    va[ks2][db].hi = __builtin_bit_cast(bf16x4, hi);
-  };
-  // Reads for S and for the first 16-key step of P V.
+__device__ __forceinline__ bf16x8 read_k(const __bf16* krow, int t) {
+  // Step t of S: key block t/8, d step t%8.
+  return *(const bf16x8*)(krow + (t >> 3) * 32 * kKStride + (t & 7) * 16);
+}
+
+__device__ __forceinline__ bf16x8 read_v(const __bf16* vs_lane, int t) {
+  // Step t of P V: 16-key step t/4, d block t%4 (two transposing reads).
+  const __bf16* src = vs_lane + (t >> 2) * 16 * kVStride + (t & 3) * 32;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * kVStride));
+  bf16x8 a;
+  a.lo = __builtin_bit_cast(bf16x4, lo);
+  a.hi = __builtin_bit_cast(bf16x4, hi);
+  return a;
+}
+
+// One MFMA phase: S^T (2 key blocks) of the wave's 32 queries against the K
+// tile whose row lq, column 8*hh is krow, and O^T += V^T P^T for the V tile
+// (vs_lane: this lane's source address for the transposing read, row
+// 4*(lane/32) + (lane/4)%4 of a 16-key step, column 16*((lane/16)%2) +
+// 4*(lane%4) of a 32-wide d block).  The 16 S steps and 16 P V steps
+// alternate; operand reads run 4 steps ahead.  The order is fixed with
+// scheduling barriers so the compiler neither serialises reads and
+// matrix-core ops nor hoists every read (which would exhaust registers).
+__device__ __forceinline__ void mfma_phase(const __bf16* krow, const __bf16* vs_lane,
+                                           const bf16x8 (&qv)[8], const bf16x8 (&pb)[4],
+                                           f32x16 (&s)[2], f32x16 (&o)[4]) {
+  constexpr int kAhead = 4;
+  bf16x8 ka[kAhead], va[kAhead];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) a[kk] = *(const bf16x8*)(krow + kk * 16);
+  for (int t = 0; t < kAhead; ++t) {
+    ka[t] = read_k(krow, t);
+    va[t] = read_v(vs_lane, t);
+  }
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
 #pragma unroll
-  for (int db = 0; db < 4; ++db) read_v(0, db);
-  __builtin_amdgcn_sched_barrier(0);
-  // S (8 chained steps) interleaved with the first P V step and with the
-  // reads for the second.
-  f32x16 s = (f32x16){};
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qv[kk], s, 0, 0, 0);
-    if (kk & 1) {
-      const int db = kk >> 1;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][db], pb[0], o[db], 0, 0, 0);
-      read_v(1, db);
+  for (int t = 0; t < 16; ++t) {
+    __builtin_amdgcn_sched_barrier(0);
+    s[t >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % kAhead], qv[t & 7], s[t >> 3], 0,
+                                                        0, 0);
+    o[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % kAhead], pb[t >> 2], o[t & 3], 0,
+                                                       0, 0);
+    if (t + kAhead < 16) {
+      ka[t % kAhead] = read_k(krow, t + kAhead);
+      va[t % kAhead] = read_v(vs_lane, t + kAhead);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][db], pb[1], o[db], 0, 0, 0);
-  return s;
 }
 
-// S^T alone (tiles whose previous tile was dead for the wave).
-__device__ __forceinline__ f32x16 qk_tile(const __bf16* ks, const bf16x8 (&qv)[8], int lq, int hh) {
-  const __bf16* krow = ks + lq * kKStride + hh * 8;
-  f32x16 s = (f32x16){};
+// S^T alone (a tile whose predecessor was dead for the wave).
+__device__ __forceinline__ void qk_tile(const __bf16* krow, const bf16x8 (&qv)[8],
+                                        f32x16 (&s)[2]) {
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + kk * 16), qv[kk], s, 0, 0,
-                                                0);
-  return s;
+  for (int t = 0; t < 16; ++t)
+    s[t >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(krow, t), qv[t & 7], s[t >> 3], 0,
+                                                        0, 0);
 }
 
 // O^T += V^T P^T alone (the last tile, and tiles dead for the wave).
-__device__ __forceinline__ void pv_tile(const __bf16* vs_lane, const bf16x8 (&pb)[2],
+__device__ __forceinline__ void pv_tile(const __bf16* vs_lane, const bf16x8 (&pb)[4],
                                         f32x16 (&o)[4]) {
 #pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const __bf16* src = vs_lane + (ks2 * 16) * kVStride + db * 32;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * kVStride));
-      bf16x8 a;
-      a.lo = __builtin_bit_cast(bf16x4, lo);
-      a.hi = __builtin_bit_cast(bf16x4, hi);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks2], o[db], 0, 0, 0);
-    }
+  for (int t = 0; t < 16; ++t)
+    o[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vs_lane, t), pb[t >> 2], o[t & 3], 0,
+                                                       0, 0);
 }
 
 __device__ __forceinline__ float lane_swap32_max(float x) {
@@ -235,15 +254,17 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const f32x4& v) {
 
 // Keys of a tile that a query cannot see become -inf: keys at or past t_end,
 // and (causal) keys after the query's global position.
-__device__ __forceinline__ void mask_tile(f32x16& s, const FwdParams& p, int64_t my_q, int64_t t0,
-                                          int64_t t_end, int hh) {
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const FwdParams& p, int64_t my_q,
+                                          int64_t t0, int64_t t_end, int hh) {
   const int64_t lim64 = min(p.causal ? p.q_pos0 + my_q - t0 : (int64_t)kN, t_end - 1 - t0);
   const int lim = (int)max(min(lim64, (int64_t)kN), (int64_t)-1) - 4 * hh;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int koff = 8 * (r >> 2) + (r & 3);
-    s[r] = koff <= lim ? s[r] : -INFINITY;
-  }
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
+      s[kb][r] = koff <= lim ? s[kb][r] : -INFINITY;
+    }
 }
 
 // Makes the compiler wait for outstanding loads into v before going on.
@@ -297,6 +318,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   // Group A streams K tiles, group B streams V tiles.
   const __bf16* my_base = group_b ? vbase : kbase;
   const int64_t my_stride = group_b ? p.v_ss : p.k_ss;
+  TileLoader ld;
+  loader_init(ld, my_stride, gtid);
+  auto tile_ptr = [&](int64_t t0) { return my_base + (t0 - p.kv_pos0) * my_stride; };
 
   // Q^T operand, resident for the whole kernel.
   bf16x8 qv[8];
@@ -319,6 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const int v_row = 4 * (lane >> 5) + ((lane >> 2) & 3);
   const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int v_lane_off = v_row * kVStride + v_col;
+  const int k_lane_off = lq * kKStride + hh * 8;
 
   f32x16 o[4];
 #pragma unroll
@@ -326,9 +351,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   float m_ref = -INFINITY;
   float l_run = 0.f;
   const float c = p.scale_log2;
-  bf16x8 pb[2];
+  bf16x8 pb[4];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int x = 0; x < 8; ++x) pb[ks][x] = (__bf16)0.f;
 
@@ -342,18 +367,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   // Prologue: K[0] and V[0] into buffer 0, zeros into V buffer 1 (read with
   // P = 0 by the first phase), tile 1 of this group's stream into registers.
   if (have) {
-    const int64_t e0 = min(t_cur.t0 + kN, t_cur.hi);
-    gload_tile(my_base, my_stride, t_cur.t0, e0, p.kv_pos0, gtid, stage);
+    gload_tile(tile_ptr(t_cur.t0), (int)(min(t_cur.t0 + kN, t_cur.hi) - t_cur.t0), ld, stage);
     if (group_b)
       lstore_tile<kVStride>(lds_v[0], gtid, stage);
     else
       lstore_tile<kKStride>(lds_k[0], gtid, stage);
     Stage zero;
-    zero.ok[0] = zero.ok[1] = false;
-    zero.x[0] = zero.x[1] = (u32x4){0u, 0u, 0u, 0u};
-    lstore_tile<kVStride>(lds_v[1], gtid, zero);
+    zero.ok = 0u;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) zero.x[i] = (u32x4){0u, 0u, 0u, 0u};
+    if (!group_b) lstore_tile<kVStride>(lds_v[1], gtid, zero);
     if (have1)
-      gload_tile(my_base, my_stride, t_n1.t0, min(t_n1.t0 + kN, t_n1.hi), p.kv_pos0, gtid, stage);
+      gload_tile(tile_ptr(t_n1.t0), (int)(min(t_n1.t0 + kN, t_n1.hi) - t_n1.t0), ld, stage);
   }
   __syncthreads();
   if (group_b) __syncthreads();  // group B runs one phase behind group A
@@ -365,7 +390,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     const int64_t t_end = min(t0 + kN, t_cur.hi);
     t_n2 = t_n1;
     const bool have2 = have1 && walk_next(p, limit, t_n2);
-
     // A tile is dead for this wave when every key of it lies after every
     // query of the wave (causal) or the wave holds no query rows: its S, P
     // and P V are skipped (P would be all zeros).
@@ -373,46 +397,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 
     // ---- MFMA phase --------------------------------------------------------
     __builtin_amdgcn_s_setprio(1);
-    f32x16 s;
+    f32x16 s[2];
+    const __bf16* krow = lds_k[jb] + k_lane_off;
+    const __bf16* vs_lane = lds_v[jb ^ 1] + v_lane_off;
     if (!dead && !dead_prev) {
-      s = mfma_phase(lds_k[jb], lds_v[jb ^ 1] + v_lane_off, qv, pb, o, lq, hh);
+      mfma_phase(krow, vs_lane, qv, pb, s, o);
     } else {
-      s = dead ? (f32x16){} : qk_tile(lds_k[jb], qv, lq, hh);
-      if (!dead_prev) pv_tile(lds_v[jb ^ 1] + v_lane_off, pb, o);
+      if (!dead) qk_tile(krow, qv, s);
+      if (!dead_prev) pv_tile(vs_lane, pb, o);
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
 
     // ---- VALU phase --------------------------------------------------------
-    if ((t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min))
-      mask_tile(s, p, my_q, t0, t_end, hh);
-    float mx = s[0];
+    if (dead) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    const float m_tile = lane_swap32_max(mx) * c;
-    // Wave-uniform decision to move the reference max.
-    const bool rescale = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kRescaleSlack) != 0;
-    if (rescale) {
-      const float m_new = fmaxf(m_ref, m_tile);
-      const float alpha = exp2_fast(m_new == m_ref ? 0.f : m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        for (int x = 0; x < 8; ++x) pb[ks][x] = (__bf16)0.f;
+    } else {
+      if ((t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min))
+        mask_tile(s, p, my_q, t0, t_end, hh);
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      const float m_tile = lane_swap32_max(mx) * c;
+      // Wave-uniform decision to move the reference max.
+      const bool rescale = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kRescaleSlack) != 0;
+      if (rescale) {
+        const float m_new = fmaxf(m_ref, m_tile);
+        const float alpha = exp2_fast(m_new == m_ref ? 0.f : m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_fast(fmaf(s[kb][r], c, -m_use));
+          s[kb][r] = e;
+          rs += e;
+        }
+      l_run += rs;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) pb[ks][x] = (__bf16)s[ks >> 1][(ks & 1) * 8 + x];
     }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = exp2_fast(fmaf(s[r], c, -m_use));
-      s[r] = e;
-      rs += e;
-    }
-    l_run += rs;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pb[ks][x] = (__bf16)s[ks * 8 + x];
     dead_prev = dead;
 
     // Stream the next tiles: group A stores K[j+1] (read from the next phase
@@ -425,10 +460,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
         lstore_tile<kKStride>(lds_k[jb ^ 1], gtid, stage);
     }
     if (have2)
-      gload_tile(my_base, my_stride, t_n2.t0, min(t_n2.t0 + kN, t_n2.hi), p.kv_pos0, gtid, stage);
+      gload_tile(tile_ptr(t_n2.t0), (int)(min(t_n2.t0 + kN, t_n2.hi) - t_n2.t0), ld, stage);
     // Finish the softmax inside this phase: without this the compiler sinks
     // the exponentials past the barrier into the next matrix-core phase.
-    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(l_run) : "memory");
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run) : "memory");
     __syncthreads();
 
     t_cur = t_n1;

@@ -279,7 +279,7 @@ def test_closed_form_zero_query_on_gpu():
 
 def test_nan_propagates():
     """A NaN value reaches every query that sees its key.  Queries of a 32-row
-    group whose rows all precede the 32-key tile holding it never touch it;
+    group whose rows all precede the 64-key tile holding it never touch it;
     inside the group that straddles that tile, causally masked rows can also
     pick it up through 0 * NaN in the P.V product (the kernel does not split
     the matrix product per row)."""
@@ -290,7 +290,7 @@ def test_nan_propagates():
     o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=2, rank=1, causal=True, q_pos0=0,
                                       out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert not torch.isnan(o[0, :, :96]).any()           # row groups that end before key 96
+    assert not torch.isnan(o[0, :, :64]).any()           # row groups that end before key 64
     assert torch.isnan(o[0, :, 100:, 5]).all()           # rows that see key 100
     keep = [d for d in range(128) if d != 5]
     assert not torch.isnan(o[0, :, :, keep]).any()       # other columns never touch it
