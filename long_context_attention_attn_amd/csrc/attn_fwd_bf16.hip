@@ -208,18 +208,7 @@ __device__ __forceinline__ void mfma_phase(const __bf16* krow, const __bf16* vs_
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// S^T alone (a tile whose predecessor was dead for the wave).
-__device__ __forceinline__ void qk_tile(const __bf16* krow, const bf16x8 (&qv)[8],
-                                        f32x16 (&s)[2]) {
-  s[0] = (f32x16){};
-  s[1] = (f32x16){};
-#pragma unroll
-  for (int t = 0; t < 16; ++t)
-    s[t >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(krow, t), qv[t & 7], s[t >> 3], 0,
-                                                        0, 0);
-}
-
-// O^T += V^T P^T alone (the last tile, and tiles dead for the wave).
+// O^T += V^T P^T alone (the last tile, after the loop).
 __device__ __forceinline__ void pv_tile(const __bf16* vs_lane, const bf16x8 (&pb)[4],
                                         f32x16 (&o)[4]) {
 #pragma unroll
@@ -228,9 +217,13 @@ __device__ __forceinline__ void pv_tile(const __bf16* vs_lane, const bf16x8 (&pb
                                                        0, 0);
 }
 
+// NaN-propagating maximum (v_maximum3_f32 on gfx950; unlike fmaxf it needs
+// no operand canonicalisation).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float lane_swap32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float lane_swap32_add(float x) {
@@ -277,9 +270,13 @@ template <typename TOut>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][kKTile];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][kVTile];
+  // All zeros: the V tile P V reads when P is known to be zero (a dead
+  // tile), so that non-finite values in a V tile no query of the wave can
+  // see never reach it through 0 * NaN.
+  __shared__ __attribute__((aligned(16))) __bf16 lds_vzero[kVTile];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in [0, 8)
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int hh = lane >> 5;
@@ -315,12 +312,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const __bf16* qbase = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
   const __bf16* kbase = (const __bf16*)p.k + b * p.k_sb + hk * p.k_sh;
   const __bf16* vbase = (const __bf16*)p.v + b * p.v_sb + hk * p.v_sh;
-  // Group A streams K tiles, group B streams V tiles.
-  const __bf16* my_base = group_b ? vbase : kbase;
-  const int64_t my_stride = group_b ? p.v_ss : p.k_ss;
+  // Group A streams K tiles, group B streams V tiles.  group_b is derived
+  // from the wave index read into a scalar register, so these selects stay
+  // scalar.
+  const __bf16* my_base_s = group_b ? vbase : kbase;
+  const int64_t my_stride_s = group_b ? p.v_ss : p.k_ss;
   TileLoader ld;
-  loader_init(ld, my_stride, gtid);
-  auto tile_ptr = [&](int64_t t0) { return my_base + (t0 - p.kv_pos0) * my_stride; };
+  loader_init(ld, my_stride_s, gtid);
+  auto tile_ptr = [&](int64_t t0) { return my_base_s + (t0 - p.kv_pos0) * my_stride_s; };
 
   // Q^T operand, resident for the whole kernel.
   bf16x8 qv[8];
@@ -364,8 +363,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   bool have1 = have && walk_next(p, limit, t_n1);
   Stage stage;
 
-  // Prologue: K[0] and V[0] into buffer 0, zeros into V buffer 1 (read with
-  // P = 0 by the first phase), tile 1 of this group's stream into registers.
+  // Prologue: K[0] and V[0] into buffer 0, the zero V tile, and tile 1 of
+  // this group's stream into registers.
   if (have) {
     gload_tile(tile_ptr(t_cur.t0), (int)(min(t_cur.t0 + kN, t_cur.hi) - t_cur.t0), ld, stage);
     if (group_b)
@@ -376,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     zero.ok = 0u;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) zero.x[i] = (u32x4){0u, 0u, 0u, 0u};
-    if (!group_b) lstore_tile<kVStride>(lds_v[1], gtid, zero);
+    if (!group_b) lstore_tile<kVStride>(lds_vzero, gtid, zero);
     if (have1)
       gload_tile(tile_ptr(t_n1.t0), (int)(min(t_n1.t0 + kN, t_n1.hi) - t_n1.t0), ld, stage);
   }
@@ -384,28 +383,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   if (group_b) __syncthreads();  // group B runs one phase behind group A
 
   int jb = 0;              // parity of tile j
-  bool dead_prev = false;  // P[j-1] is all zeros (tile j-1 dead for this wave)
+  bool dead_prev = true;   // P[j-1] is all zeros (no tile before the first)
   while (have) {
     const int64_t t0 = t_cur.t0;
     const int64_t t_end = min(t0 + kN, t_cur.hi);
     t_n2 = t_n1;
     const bool have2 = have1 && walk_next(p, limit, t_n2);
     // A tile is dead for this wave when every key of it lies after every
-    // query of the wave (causal) or the wave holds no query rows: its S, P
-    // and P V are skipped (P would be all zeros).
+    // query of the wave (causal) or the wave holds no query rows: its
+    // softmax is skipped, P = 0, and its P V reads the zero tile.  (The
+    // matrix-core ops still run: a branch around them costs more in register
+    // copies than it saves.)
     const bool dead = (p.causal && t0 > wave_qpos_max) || wave_q0 >= p.seq_q;
 
     // ---- MFMA phase --------------------------------------------------------
     __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
     const __bf16* krow = lds_k[jb] + k_lane_off;
-    const __bf16* vs_lane = lds_v[jb ^ 1] + v_lane_off;
-    if (!dead && !dead_prev) {
-      mfma_phase(krow, vs_lane, qv, pb, s, o);
-    } else {
-      if (!dead) qk_tile(krow, qv, s);
-      if (!dead_prev) pv_tile(vs_lane, pb, o);
-    }
+    const __bf16* vs_lane = (dead_prev ? lds_vzero : lds_v[jb ^ 1]) + v_lane_off;
+    mfma_phase(krow, vs_lane, qv, pb, s, o);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
 
@@ -418,9 +414,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     } else {
       if ((t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min))
         mask_tile(s, p, my_q, t0, t_end, hh);
-      float mx = fmaxf(s[0][0], s[1][0]);
+      float mx0 = s[0][0], mx1 = s[1][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      for (int r = 1; r < 15; r += 2) {
+        mx0 = vmax(vmax(mx0, s[0][r]), s[0][r + 1]);
+        mx1 = vmax(vmax(mx1, s[1][r]), s[1][r + 1]);
+      }
+      const float mx = vmax(vmax(mx0, s[0][15]), vmax(mx1, s[1][15]));
       const float m_tile = lane_swap32_max(mx) * c;
       // Wave-uniform decision to move the reference max.
       const bool rescale = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kRescaleSlack) != 0;
@@ -433,16 +433,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
       }
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float rs = 0.f;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no serial add chain
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float e = exp2_fast(fmaf(s[kb][r], c, -m_use));
           s[kb][r] = e;
-          rs += e;
+          rs[r & 3] += e;
         }
-      l_run += rs;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   if (!group_b) __syncthreads();  // match group B's extra barrier
 
   // The last tile's P V: V[T-1] sits in buffer jb ^ 1.
-  if (!dead_prev) pv_tile(lds_v[jb ^ 1] + v_lane_off, pb, o);
+  pv_tile((dead_prev ? lds_vzero : lds_v[jb ^ 1]) + v_lane_off, pb, o);
 
   // Finalise: O = acc / l, LSE = (m_ref + log2 l) ln 2; l == 0 means no
   // visible key (O = 0, LSE = -inf).  NaN in l propagates.
