@@ -56,7 +56,8 @@ typedef enum { SHATTN_BF16 = 0, SHATTN_F32 = 1 } shattn_dtype;
  * Q is [batch, heads_q, seq_q, head_dim]; K and V are
  * [batch, heads_kv, seq_kv, head_dim]; O is [batch, heads_q, seq_q, head_dim].
  * Strides are in ELEMENTS of the tensor's own dtype, for the (batch, head,
- * sequence) axes; the head_dim axis must be contiguous (stride 1).
+ * sequence) axes; the head_dim axis must be contiguous (stride 1).  A
+ * sequence stride above 2^24 elements is refused with SHATTN_EUNSUPPORTED.
  *
  * Query head h reads KV head h / (heads_q / heads_kv) (contiguous GQA
  * groups; heads_q == heads_kv is MHA).

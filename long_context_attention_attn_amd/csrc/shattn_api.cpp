@@ -18,6 +18,10 @@ using shattn::FwdParams;
 
 constexpr int32_t kSupportedHeadDim = 128;
 constexpr int64_t kPosLimit = (int64_t)1 << 60;  // keeps position arithmetic far from overflow
+// The kernels address rows within one 64-row tile in 32-bit arithmetic
+// (row * seq_stride + column), so a sequence stride must stay below 2^24
+// elements.  Real layouts ([B, H, S, D] or [B, S, H, D]) are far below it.
+constexpr int64_t kSeqStrideLimit = (int64_t)1 << 24;
 
 bool valid_dtype(int32_t d) { return d == SHATTN_BF16 || d == SHATTN_F32; }
 
@@ -54,6 +58,9 @@ int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v
   if (!strides_ok(d->q_stride, es) || !strides_ok(d->k_stride, es) ||
       !strides_ok(d->v_stride, es) || !strides_ok(d->o_stride, o_esize))
     return SHATTN_EINVAL;
+  if (d->q_stride[2] > kSeqStrideLimit || d->k_stride[2] > kSeqStrideLimit ||
+      d->v_stride[2] > kSeqStrideLimit || d->o_stride[2] > kSeqStrideLimit)
+    return SHATTN_EUNSUPPORTED;
   const bool q_empty = d->batch == 0 || d->seq_q == 0;
   const bool kv_empty = d->batch == 0 || kv_rows == 0;
   if (!q_empty && (q == nullptr || o == nullptr || lse == nullptr)) return SHATTN_EINVAL;

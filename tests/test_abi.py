@@ -96,6 +96,10 @@ S3 = ctypes.c_int64 * 3
     ({"q_stride": S3(1, 1, 129)}, 1),   # row stride not a multiple of 16 bytes
     ({"k_stride": S3(-128, 128, 128)}, 1),
     ({"o_stride": S3(4, 4, 4)}, 1),
+    ({"k_stride": S3(0, 0, (1 << 24) + 8)}, 2),   # row stride beyond 2^24 elements
+    ({"v_stride": S3(0, 0, (1 << 24) + 8)}, 2),
+    ({"q_stride": S3(0, 0, (1 << 24) + 8)}, 2),
+    ({"o_stride": S3(0, 0, (1 << 24) + 8)}, 2),
 ])
 def test_shifted_rejects_bad_desc(case, expect):
     lib = _lib()
