@@ -39,6 +39,9 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["long_context_attention_attn_amd/csrc/attn_fwd_bf16.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_{workload}_traffic.json")
+# torch's negation kernel serves as the calibration copy: it reads and writes
+# each element once.
+CALIB_KERNEL = "neg_kernel"
 METRIC = "attention TFLOP/s per MI355X + % bf16 MFMA peak, 32K-ctx GQA rank shard"
 
 
@@ -110,39 +113,40 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     }
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, out: str, workload: str, copy_mib: int):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention
-    kernel, scaled by what the same counters read for the calibration copy."""
+def summarize_pmc(fetch_dir: str, write_dir: str, out: str, workload: str, copy_mib: int):
+    """HBM bytes per launch of the attention kernel from two rocprofv3 --pmc
+    runs of this script with --calib-copy-mib (FETCH_SIZE, then WRITE_SIZE).
 
-    def per_kernel(path, counter):
-        vals = {}
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter:
-                    continue
-                name = row.get("Kernel_Name", "")
-                vals.setdefault(name, []).append(float(row["Counter_Value"]))
-        return vals
+    rocprofv3 writes one CSV row per counter instance; a dispatch's value is
+    the sum of its rows (KiB).  The attention kernel's mean per dispatch is
+    scaled by bytes / reading of the calibration kernel, which reads and
+    writes exactly ``copy_mib`` MiB."""
+    import glob
 
-    def pick(vals, needle):
-        hits = [v for n, v in vals.items() if needle in n]
-        if not hits:
-            raise SystemExit(f"no kernel matching {needle!r} in counters")
-        flat = [x for v in hits for x in v]
-        return sum(flat) / len(flat)
+    def per_dispatch(root, counter, needle):
+        sums = {}
+        for path in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter or needle not in row.get("Kernel_Name", ""):
+                        continue
+                    key = (path, row["Dispatch_Id"])
+                    sums[key] = sums.get(key, 0.0) + float(row["Counter_Value"])
+        if not sums:
+            raise SystemExit(f"no {counter} rows for a kernel matching {needle!r} under {root}")
+        return sum(sums.values()) / len(sums) * 1024.0, len(sums)
 
-    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
-    write = per_kernel(write_csv, "WRITE_SIZE")
+    f_attn, n_fa = per_dispatch(fetch_dir, "FETCH_SIZE", "attn_fwd")
+    w_attn, n_wa = per_dispatch(write_dir, "WRITE_SIZE", "attn_fwd")
+    f_copy, _ = per_dispatch(fetch_dir, "FETCH_SIZE", CALIB_KERNEL)
+    w_copy, _ = per_dispatch(write_dir, "WRITE_SIZE", CALIB_KERNEL)
     copy_bytes = copy_mib * 2**20
-    f_attn = pick(fetch, "attn_fwd_kernel") * 1024
-    w_attn = pick(write, "attn_fwd_kernel") * 1024
-    f_copy = pick(fetch, "copy") * 1024
-    w_copy = pick(write, "copy") * 1024
     f_scale = copy_bytes / f_copy
     w_scale = copy_bytes / w_copy
     rec = {
         "workload": workload,
         "kernel_sha": kernel_hash(),
+        "dispatches": [n_fa, n_wa],
         "fetch_bytes_raw": f_attn,
         "write_bytes_raw": w_attn,
         "copy_bytes": copy_bytes,
@@ -166,7 +170,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0)
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--flush-mib", type=int, default=0)
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -208,13 +213,25 @@ def main():
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    if args.flush_mib:
+        scratch = torch.empty(args.flush_mib * 2**20 // 4, dtype=torch.float32, device=dev)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.fill_(float(i))
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / max(args.steps, 1)
+    else:
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
     t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.4f} ms/step ({t_wall:.3f} s wall), {tflops:.1f} TFLOP/s")
@@ -224,7 +241,7 @@ def main():
         src.fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     is_f32 = w.dtype == "f32"
@@ -250,6 +267,7 @@ def main():
             "seq_kv": w.seq_kv, "num_chunks": w.num_chunks, "rank": w.rank,
             "causal": w.causal, "algorithmic_gflop": round(flops / 1e9, 3),
             "parallelism": "one rank's shard on 1 GPU",
+            "cache_flush_mib": args.flush_mib,
         },
         "roofline": {
             "bound": "mfma",
