@@ -1,22 +1,25 @@
-// Fused shifted-chunk attention forward for gfx950 (CDNA4).
+// Fused shifted-chunk attention forward for gfx950 (CDNA4), fp32 inputs.
 //
 // One workgroup owns kBlockM = 128 query rows of one (batch, query head):
 // four waves of 32 rows each.  It walks the KV chunks in the rank-shifted
 // order c_j = (j + rank) % J (the `shift` primitive of CommIR, papers.lqhl.me
 // summary "Mercury (SOSP 2025)", section 核心方法), streaming each chunk's
-// key/value tiles through a double-buffered LDS stage, and carries the
-// online-softmax state (running max m, running sum l, unnormalised output)
-// in registers across chunk boundaries.  Rescaling the state at a chunk
-// boundary is exactly the log-sum-exp merge of that chunk's partial result,
-// so the fused loop computes what attn_chunk_fwd + lse_merge compute, in one
-// launch.  Chunk ranges that are causally invisible to the whole workgroup
-// are skipped without touching memory.
+// key/value tiles (32 keys) through a double-buffered LDS stage, and carries
+// the online-softmax state (running max m, running sum l, unnormalised
+// output) in registers across chunk boundaries.  Rescaling the state at a
+// chunk boundary is exactly the log-sum-exp merge of that chunk's partial
+// result, so the fused loop computes what attn_chunk_fwd + lse_merge compute,
+// in one launch.  Chunk ranges that are causally invisible to the whole
+// workgroup are skipped without touching memory.
+//
+// Every product and sum stays in fp32 (v_mfma_f32_32x32x2_f32); this path
+// exists for fp32 callers and small problems, not for throughput.
 //
 // Matrix-core mapping (per wave, 32 queries):
-//   S^T[key][q] = sum_d K[key][d] Q[q][d]     v_mfma_f32_32x32x16_bf16
+//   S^T[key][q] = sum_d K[key][d] Q[q][d]
 //     A = K tile rows from LDS, B = Q^T held in VGPRs for the whole kernel.
 //   O^T[d][q]  += sum_key V^T[d][key] P^T[key][q]
-//     A = V^T from LDS (stored transposed), B = P^T straight from the S^T
+//     A = V from LDS (row-major, read per key), B = P^T straight from the S^T
 //     accumulator registers (no cross-lane traffic).
 // With S^T in the accumulator each lane owns one query column, so the row
 // max / row sum are in-lane reductions plus one exchange with the partner
@@ -24,12 +27,6 @@
 //
 // Accumulator layout of a 32x32 MFMA (lane l, register r):
 //   column = l % 32, row = 8*(r/4) + 4*(l/32) + (r%4).
-// The contraction index order inside A and B operands is the same for both,
-// so any consistent assignment of keys to (lane half, slot) is valid; the
-// V^T rows in LDS are written in the key order the P^T registers carry.
-//
-// The fp32 path (F32 inputs) uses v_mfma_f32_32x32x2_f32 with the same
-// structure and keeps every value in fp32.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -40,22 +37,10 @@
 namespace shattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <bool C, typename A, typename B>
-struct Pick {
-  typedef A type;
-};
-template <typename A, typename B>
-struct Pick<false, A, B> {
-  typedef B type;
-};
 
 constexpr int kHeadDim = 128;
 constexpr int kWaves = 4;
@@ -63,27 +48,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kBlockMF32;
 static_assert(kBlockM == kWaves * 32, "one wave per 32 query rows");
 
-// Tile geometry per input type.
-template <typename T>
-struct Tile;
-
-template <>
-struct Tile<__bf16> {
-  static constexpr int kN = 64;              // keys per tile
-  static constexpr int kKStride = 136;       // K row stride in LDS (elements), +16 B pad
-  static constexpr int kVStride = kN + 8;    // V^T row stride in LDS (elements), +16 B pad
-  static constexpr int kKElems = kN * kKStride;
-  static constexpr int kVElems = kHeadDim * kVStride;
-};
-
-template <>
-struct Tile<float> {
-  static constexpr int kN = 32;
-  static constexpr int kKStride = 130;       // 2 floats pad: lanes (row, d parity) hit distinct banks
-  static constexpr int kVStride = 136;       // V kept row-major [key][d]
-  static constexpr int kKElems = kN * kKStride;
-  static constexpr int kVElems = kN * kVStride;
-};
+// Tile geometry: 32 keys per tile; K and V row-major in LDS.
+constexpr int kN = 32;
+constexpr int kKStride = 130;  // 2 floats pad: lanes (row, d parity) hit distinct banks
+constexpr int kVStride = 136;
+constexpr int kKElems = kN * kKStride;
+constexpr int kVElems = kN * kVStride;
 
 // Visit-order walker over KV tiles: chunk c_j = (j + rank) % J, clipped to the
 // keys the workgroup can see (limit = one past its largest query position
@@ -128,67 +98,8 @@ __device__ __forceinline__ bool walk_next(const FwdParams& p, int64_t limit, Til
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------
-// Global -> register staging and register -> LDS stores, per input type.
+// Global -> register staging and register -> LDS stores.
 // ----------------------------------------------------------------------------
-
-// bf16: K tile is 64 rows x 256 B = 1024 16-byte pieces, 4 per thread, row-major
-// in LDS.  V tile: each thread loads 4 consecutive keys x 8 dims and writes
-// them transposed (V^T[d][key]) with keys permuted inside each 16-key group so
-// that a lane's 8 B-operand keys are contiguous.
-struct StageBf16 {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-__device__ __forceinline__ void gload_bf16(const FwdParams& p, const __bf16* kb,
-                                           const __bf16* vb, int64_t t0, int64_t t_end,
-                                           int tid, StageBf16& s) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int id = tid + kThreads * i;
-    int row = id >> 4, ch = id & 15;
-    int64_t key = t0 + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < t_end) x = *(const u32x4*)(kb + (key - p.kv_pos0) * p.k_ss + ch * 8);
-    s.k[i] = x;
-  }
-  int dc = tid & 15, kg = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int64_t key = t0 + kg * 4 + i;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < t_end) x = *(const u32x4*)(vb + (key - p.kv_pos0) * p.v_ss + dc * 8);
-    s.v[i] = x;
-  }
-}
-
-__device__ __forceinline__ void lstore_bf16(__bf16* ks, __bf16* vt, int tid, const StageBf16& s) {
-  using T = Tile<__bf16>;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int id = tid + kThreads * i;
-    int row = id >> 4, ch = id & 15;
-    *(u32x4*)(ks + row * T::kKStride + ch * 8) = s.k[i];
-  }
-  int dc = tid & 15, kg = tid >> 4;
-  int gi = kg & 3;
-  // Position of key group gi (4 keys) inside its 16-key group: 0, 8, 4, 12.
-  int col = (kg >> 2) * 16 + ((gi & 1) << 3) + ((gi >> 1) << 2);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    int w = e >> 1;
-    uint32_t a0 = s.v[0][w], a1 = s.v[1][w], a2 = s.v[2][w], a3 = s.v[3][w];
-    u32x2 out;
-    if (e & 1) {
-      out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-      out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-    } else {
-      out[0] = (a0 & 0xffffu) | (a1 << 16);
-      out[1] = (a2 & 0xffffu) | (a3 << 16);
-    }
-    *(u32x2*)(vt + (dc * 8 + e) * T::kVStride + col) = out;
-  }
-}
 
 // fp32: K and V tiles are 32 rows x 512 B = 1024 16-byte pieces each, 4 per
 // thread; both stay row-major in LDS.
@@ -216,16 +127,15 @@ __device__ __forceinline__ void gload_f32(const FwdParams& p, const float* kb, c
 }
 
 __device__ __forceinline__ void lstore_f32(float* ks, float* vs, int tid, const StageF32& s) {
-  using T = Tile<float>;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int id = tid + kThreads * i;
     int row = id >> 5, ch = id & 31;
     f32x2 lo = {s.k[i][0], s.k[i][1]};
     f32x2 hi = {s.k[i][2], s.k[i][3]};
-    *(f32x2*)(ks + row * T::kKStride + ch * 4) = lo;
-    *(f32x2*)(ks + row * T::kKStride + ch * 4 + 2) = hi;
-    *(f32x4*)(vs + row * T::kVStride + ch * 4) = s.v[i];
+    *(f32x2*)(ks + row * kKStride + ch * 4) = lo;
+    *(f32x2*)(ks + row * kKStride + ch * 4 + 2) = hi;
+    *(f32x4*)(vs + row * kVStride + ch * 4) = s.v[i];
   }
 }
 
@@ -248,15 +158,11 @@ __device__ __forceinline__ void store_row4<__bf16>(__bf16* dst, float a, float b
 // ----------------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------------
-template <typename TIn, typename TOut>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
-  using T = Tile<TIn>;
-  constexpr int kN = T::kN;
-  constexpr int kNKB = kN / 32;  // 32-key blocks per tile
-  constexpr bool kBf16 = __is_same(TIn, __bf16);
+template <typename TOut>
+__global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(FwdParams p) {
 
-  __shared__ __attribute__((aligned(16))) TIn lds_k[2][T::kKElems];
-  __shared__ __attribute__((aligned(16))) TIn lds_v[2][T::kVElems];
+  __shared__ __attribute__((aligned(16))) float lds_k[2][kKElems];
+  __shared__ __attribute__((aligned(16))) float lds_v[2][kVElems];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -284,29 +190,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   const int64_t wave_qpos_max = p.q_pos0 + wave_last_q;
   const int64_t limit = p.causal ? p.q_pos0 + q_start + q_rows_wg : INT64_MAX;
 
-  const TIn* qb = (const TIn*)p.q + b * p.q_sb + h * p.q_sh;
-  const TIn* kbase = (const TIn*)p.k + b * p.k_sb + hk * p.k_sh;
-  const TIn* vbase = (const TIn*)p.v + b * p.v_sb + hk * p.v_sh;
+  const float* qb = (const float*)p.q + b * p.q_sb + h * p.q_sh;
+  const float* kbase = (const float*)p.k + b * p.k_sb + hk * p.k_sh;
+  const float* vbase = (const float*)p.v + b * p.v_sb + hk * p.v_sh;
 
   // Q^T B-operands, resident for the whole kernel.
-  constexpr int kQRegs = kBf16 ? 8 : 64;
-  typedef typename Pick<kBf16, bf16x8, float>::type QOp;
-  QOp qv[kQRegs];
-  if constexpr (kBf16) {
+  // Lane half hh holds the odd (hh = 1) or even d of each pair of the
+  // 2-deep fp32 contraction.
+  float qv[64];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *(const u32x4*)(qb + my_q * p.q_ss + kk * 16 + hh * 8);
-      qv[kk] = __builtin_bit_cast(bf16x8, x);
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) x = *(const f32x4*)(qb + my_q * p.q_ss + c * 4);
-      qv[2 * c] = hh ? x[1] : x[0];
-      qv[2 * c + 1] = hh ? x[3] : x[2];
-    }
+  for (int c = 0; c < 32; ++c) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (row_ok) x = *(const f32x4*)(qb + my_q * p.q_ss + c * 4);
+    qv[2 * c] = hh ? x[1] : x[0];
+    qv[2 * c + 1] = hh ? x[3] : x[2];
   }
 
   f32x16 acc[4];
@@ -316,20 +213,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   float l_run = 0.f;        // this lane's half of the running sum
   const float sl2 = p.scale_log2;
 
-  typedef typename Pick<kBf16, StageBf16, StageF32>::type Stage;
-  Stage st;
+  StageF32 st;
 
   TileWalk cur;
   bool have = walk_from(p, 0, limit, cur);
   if (have) {
     int64_t t_end = min(cur.t0 + kN, cur.hi);
-    if constexpr (kBf16) {
-      gload_bf16(p, kbase, vbase, cur.t0, t_end, tid, st);
-      lstore_bf16(lds_k[0], lds_v[0], tid, st);
-    } else {
-      gload_f32(p, kbase, vbase, cur.t0, t_end, tid, st);
-      lstore_f32(lds_k[0], lds_v[0], tid, st);
-    }
+    gload_f32(p, kbase, vbase, cur.t0, t_end, tid, st);
+    lstore_f32(lds_k[0], lds_v[0], tid, st);
   }
   __syncthreads();
 
@@ -341,107 +232,65 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
     const bool have_next = walk_next<kN>(p, limit, nxt);
     if (have_next) {
       int64_t n_end = min(nxt.t0 + kN, nxt.hi);
-      if constexpr (kBf16)
-        gload_bf16(p, kbase, vbase, nxt.t0, n_end, tid, st);
-      else
-        gload_f32(p, kbase, vbase, nxt.t0, n_end, tid, st);
+      gload_f32(p, kbase, vbase, nxt.t0, n_end, tid, st);
     }
 
     // Skip waves whose every query precedes the whole tile (causal) or that
     // hold no query rows at all.
     const bool wave_work = wave_live && (!p.causal || t0 <= wave_qpos_max);
     if (wave_work) {
-      const TIn* ks = lds_k[buf];
-      const TIn* vs = lds_v[buf];
-      f32x16 s[kNKB];
+      const float* ks = lds_k[buf];
+      const float* vs = lds_v[buf];
+      f32x16 s = {};
 #pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb) {
-        s[kb] = (f32x16){};
-        if constexpr (kBf16) {
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 a = *(const bf16x8*)(ks + (kb * 32 + lq) * T::kKStride + kk * 16 + hh * 8);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[kk], s[kb], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 64; ++kk) {
-            float a = ks[(kb * 32 + lq) * T::kKStride + 2 * kk + hh];
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qv[kk], s[kb], 0, 0, 0);
-          }
-        }
+      for (int kk = 0; kk < 64; ++kk) {
+        float a = ks[lq * kKStride + 2 * kk + hh];
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qv[kk], s, 0, 0, 0);
       }
 
       // Mask: keys past the tile end, and (causal) keys after the query.
       const bool need_mask = (t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min);
       if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int64_t key = t0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            bool ok = key < t_end && (!p.causal || key <= qpos);
-            s[kb][r] = ok ? s[kb][r] : -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          int64_t key = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          bool ok = key < t_end && (!p.causal || key <= qpos);
+          s[r] = ok ? s[r] : -INFINITY;
         }
       }
 
       // Online softmax in log2 units.
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx * sl2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = fast_exp2(fmaf(s[kb][r], sl2, -m_use));
-          s[kb][r] = e;
-          rs += e;
-        }
+      for (int r = 0; r < 16; ++r) {
+        float e = fast_exp2(fmaf(s[r], sl2, -m_use));
+        s[r] = e;
+        rs += e;
+      }
       l_run = fmaf(l_run, alpha, rs);
       m_run = m_new;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
 
       // O^T += V^T P^T.
-      if constexpr (kBf16) {
-        bf16x8 pb[4];
 #pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int x = 0; x < 8; ++x) pb[ks4][x] = (__bf16)s[ks4 >> 1][(ks4 & 1) * 8 + x];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int ks4 = 0; ks4 < 4; ++ks4) {
-            bf16x8 a = *(const bf16x8*)(vs + (db * 32 + lq) * T::kVStride + ks4 * 16 + hh * 8);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks4], acc[db], 0, 0, 0);
-          }
-      } else {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int key = 8 * (r >> 2) + 4 * hh + (r & 3);
-            float a = vs[key * T::kVStride + db * 32 + lq];
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[0][r], acc[db], 0, 0, 0);
-          }
-      }
+        for (int r = 0; r < 16; ++r) {
+          int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+          float a = vs[key * kVStride + db * 32 + lq];
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], acc[db], 0, 0, 0);
+        }
     }
 
-    if (have_next) {
-      if constexpr (kBf16)
-        lstore_bf16(lds_k[buf ^ 1], lds_v[buf ^ 1], tid, st);
-      else
-        lstore_f32(lds_k[buf ^ 1], lds_v[buf ^ 1], tid, st);
-    }
+    if (have_next) lstore_f32(lds_k[buf ^ 1], lds_v[buf ^ 1], tid, st);
     __syncthreads();
     buf ^= 1;
     cur = nxt;
@@ -468,21 +317,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename TIn, typename TOut>
+template <typename TOut>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
   int64_t blocks = (int64_t)p.num_q_tiles * p.batch * p.heads_q;
   if (blocks == 0) return hipSuccess;
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel((const void*)&attn_fwd_kernel<TIn, TOut>, dim3((unsigned)blocks),
+  return hipLaunchKernel((const void*)&attn_fwd_f32_kernel<TOut>, dim3((unsigned)blocks),
                          dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(const FwdParams& p, DType out, hipStream_t stream) {
-  return out == DType::BF16 ? launch_typed<float, __bf16>(p, stream)
-                            : launch_typed<float, float>(p, stream);
+  return out == DType::BF16 ? launch_typed<__bf16>(p, stream)
+                            : launch_typed<float>(p, stream);
 }
 
 hipError_t launch_attn_fwd(const FwdParams& p, DType in, DType out, hipStream_t stream) {
