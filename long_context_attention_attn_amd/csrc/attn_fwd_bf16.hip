@@ -449,28 +449,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 #pragma unroll
   for (int r = 0; r < 16; ++r) s_hi[r] = -INFINITY;
   float m_use = 0.f;
-  while (have) {
-    const int64_t t0 = t_cur.t0;
-    const int64_t t_end = min(t0 + kN, t_cur.hi);
-    t_n3 = t_n2;
-    const bool have3 = have2 && walk_next(p, limit, t_n3);
-    // A tile is dead for this wave when every key of it lies after every
-    // query of the wave (causal) or the wave holds no query rows: its
-    // softmax is skipped, P = 0, and its P V reads the zero tile.  (The
-    // matrix-core ops still run: a branch around them costs more in register
-    // copies than it saves.)
-    const bool dead = (p.causal && t0 > wave_qpos_max) || wave_q0 >= p.seq_q;
+  // The hot loop below modifies O only through the matrix-core ops: a tile
+  // whose scores would move the reference max leaves it, and the outer loop
+  // rescales O and finishes that tile.  (Rescaling inside the loop makes the
+  // compiler keep two register copies of O and move all 64 values between
+  // them twice per tile.)
+  f32x16 s[2];
+  int64_t t0 = 0, t_end = 0;
+  bool dead = true, have3 = false;
+  float m_tile = -INFINITY;
 
-    // ---- MFMA phase --------------------------------------------------------
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2];
-    const __bf16* ktile = &lds_k[slot][0];
-    const __bf16* vtile = dead_prev ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
-    l_run += mfma_phase(ktile, vtile, koff, voff, qv, pb, s_hi, c, m_use, s, o);
-    __builtin_amdgcn_s_setprio(0);
-    phase_barrier();
-
-    // ---- VALU phase --------------------------------------------------------
+  // Second part of the VALU phase: exponentials of key block 0 (or P = 0
+  // for a dead tile), the copy of tile j+3, the wait for tile j+1, the
+  // barrier, and the rotation of the tile window.
+  auto valu_rest = [&]() __attribute__((always_inline)) {
     if (dead) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -480,26 +472,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
       for (int r = 0; r < 16; ++r) s_hi[r] = -INFINITY;
       m_use = 0.f;
     } else {
-      if ((t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min))
-        mask_tile(s, p.causal != 0, wave_qpos_min - t0, t0, t_end, lq, hh);
-      float mx0 = s[0][0], mx1 = s[1][0];
-#pragma unroll
-      for (int r = 1; r < 15; r += 2) {
-        mx0 = vmax(vmax(mx0, s[0][r]), s[0][r + 1]);
-        mx1 = vmax(vmax(mx1, s[1][r]), s[1][r + 1]);
-      }
-      const float mx = vmax(vmax(mx0, s[0][15]), vmax(mx1, s[1][15]));
-      const float m_tile = lane_swap32_max(mx) * c;
-      // Wave-uniform decision to move the reference max.
-      const bool rescale = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kRescaleSlack) != 0;
-      if (rescale) {
-        const float m_new = fmaxf(m_ref, m_tile);
-        const float alpha = exp2_fast(m_new == m_ref ? 0.f : m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      }
       m_use = m_ref == -INFINITY ? 0.f : m_ref;
       // First half (key block 0) now; key block 1 in the next MFMA phase.
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -534,6 +506,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     t_n2 = t_n3;
     have2 = have3;
     slot = (slot + 1) & (kRing - 1);
+  };
+
+  while (have) {
+    bool move_ref = false;
+    do {
+      t0 = t_cur.t0;
+      t_end = min(t0 + kN, t_cur.hi);
+      t_n3 = t_n2;
+      have3 = have2 && walk_next(p, limit, t_n3);
+      // A tile is dead for this wave when every key of it lies after every
+      // query of the wave (causal) or the wave holds no query rows: its
+      // softmax is skipped, P = 0, and its P V reads the zero tile.  (The
+      // matrix-core ops still run: a branch around them costs more in
+      // register copies than it saves.)
+      dead = (p.causal && t0 > wave_qpos_max) || wave_q0 >= p.seq_q;
+
+      // ---- MFMA phase ------------------------------------------------------
+      __builtin_amdgcn_s_setprio(1);
+      const __bf16* ktile = &lds_k[slot][0];
+      const __bf16* vtile = dead_prev ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
+      l_run += mfma_phase(ktile, vtile, koff, voff, qv, pb, s_hi, c, m_use, s, o);
+      __builtin_amdgcn_s_setprio(0);
+      phase_barrier();
+
+      // ---- VALU phase ------------------------------------------------------
+      if (!dead) {
+        if ((t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min))
+          mask_tile(s, p.causal != 0, wave_qpos_min - t0, t0, t_end, lq, hh);
+        float mx0 = s[0][0], mx1 = s[1][0];
+#pragma unroll
+        for (int r = 1; r < 15; r += 2) {
+          mx0 = vmax(vmax(mx0, s[0][r]), s[0][r + 1]);
+          mx1 = vmax(vmax(mx1, s[1][r]), s[1][r + 1]);
+        }
+        const float mx = vmax(vmax(mx0, s[0][15]), vmax(mx1, s[1][15]));
+        m_tile = lane_swap32_max(mx) * c;
+        // Wave-uniform decision to move the reference max.
+        move_ref = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kRescaleSlack) != 0;
+        if (move_ref) break;
+      }
+      valu_rest();
+    } while (have);
+    if (!move_ref) break;
+    // Rare: move the reference max of this tile's rows and rescale O and l.
+    {
+      const float m_new = fmaxf(m_ref, m_tile);
+      const float alpha = exp2_fast(m_new == m_ref ? 0.f : m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    valu_rest();
   }
   if (!group_b) phase_barrier();  // match group B's extra barrier
 
