@@ -57,7 +57,8 @@ typedef enum { SHATTN_BF16 = 0, SHATTN_F32 = 1 } shattn_dtype;
  * [batch, heads_kv, seq_kv, head_dim]; O is [batch, heads_q, seq_q, head_dim].
  * Strides are in ELEMENTS of the tensor's own dtype, for the (batch, head,
  * sequence) axes; the head_dim axis must be contiguous (stride 1).  A
- * sequence stride above 2^24 elements is refused with SHATTN_EUNSUPPORTED.
+ * sequence stride above 2^24 elements, or more than 2^31 - 64 key rows in one
+ * call (kv_len, kv_len_total), is refused with SHATTN_EUNSUPPORTED.
  *
  * Query head h reads KV head h / (heads_q / heads_kv) (contiguous GQA
  * groups; heads_q == heads_kv is MHA).

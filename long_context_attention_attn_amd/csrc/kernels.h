@@ -31,6 +31,12 @@ struct FwdParams {
   int32_t causal;
   float scale_log2;  // softmax scale times log2(e)
   int32_t num_q_tiles;
+  // The same walk relative to key row 0 of the buffer: its row count
+  // (< 2^31), the first row of the visit order (rank * chunk_len), and
+  // q_pos0 - kv_pos0 (the position of query row 0 relative to key row 0).
+  int32_t kv_rows;
+  int32_t seg_a0;
+  int64_t q_rel0;
 };
 
 enum class DType : int { BF16 = 0, F32 = 1 };

@@ -22,6 +22,8 @@ constexpr int64_t kPosLimit = (int64_t)1 << 60;  // keeps position arithmetic fa
 // (row * seq_stride + column), so a sequence stride must stay below 2^24
 // elements.  Real layouts ([B, H, S, D] or [B, S, H, D]) are far below it.
 constexpr int64_t kSeqStrideLimit = (int64_t)1 << 24;
+// Key rows of one call: the kernels index them in 32-bit arithmetic.
+constexpr int64_t kKvRowLimit = ((int64_t)1 << 31) - 64;
 
 bool valid_dtype(int32_t d) { return d == SHATTN_BF16 || d == SHATTN_F32; }
 
@@ -119,11 +121,15 @@ int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const 
     return SHATTN_EINVAL;
   int st = check_desc(desc, q, k, v, o_part, lse_part, kv_len, 4);
   if (st != SHATTN_OK) return st;
+  if (kv_len > kKvRowLimit) return SHATTN_EUNSUPPORTED;
   FwdParams p = make_params(desc, q, k, v, o_part, lse_part);
   p.kv_pos0 = kv_pos0;
   p.chunk_len = kv_len;
   p.num_chunks = 1;
   p.rank = 0;
+  p.kv_rows = (int32_t)kv_len;
+  p.seg_a0 = 0;
+  p.q_rel0 = desc->q_pos0 - kv_pos0;
   if (desc->batch == 0 || desc->seq_q == 0) return SHATTN_OK;
   return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, DType::F32, stream));
 }
@@ -157,11 +163,15 @@ int attn_shifted_fwd(const shattn_desc* desc, const void* q, const void* k, cons
   if (desc == nullptr || !valid_dtype(desc->out_dtype)) return SHATTN_EINVAL;
   int st = check_desc(desc, q, k, v, o, lse, kv_len_total, elem_size(desc->out_dtype));
   if (st != SHATTN_OK) return st;
+  if (kv_len_total > kKvRowLimit) return SHATTN_EUNSUPPORTED;
   FwdParams p = make_params(desc, q, k, v, o, lse);
   p.kv_pos0 = 0;
   p.chunk_len = kv_len_total / num_chunks;
   p.num_chunks = num_chunks;
   p.rank = rank;
+  p.kv_rows = (int32_t)kv_len_total;
+  p.seg_a0 = (int32_t)(p.chunk_len * rank);
+  p.q_rel0 = desc->q_pos0;
   if (desc->batch == 0 || desc->seq_q == 0) return SHATTN_OK;
   return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, (DType)desc->out_dtype,
                                            stream));

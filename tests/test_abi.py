@@ -123,6 +123,8 @@ def test_shifted_rejects_bad_arguments():
     assert _shifted(lib, d, q=FAKE + 8) == 1      # misaligned
     assert _shifted(lib, d, o=FAKE + 4) == 1
     assert _shifted(lib, d, lse=FAKE + 2) == 1
+    # KV rows are indexed in 32-bit arithmetic: more than 2^31 - 64 is refused.
+    assert _shifted(lib, d, total=(1 << 31) - 56, nch=8) == 2
 
 
 def test_chunk_rejects_bad_arguments():
@@ -134,6 +136,7 @@ def test_chunk_rejects_bad_arguments():
     assert _chunk(lib, d, k=0) == 1
     assert _chunk(lib, d, v=FAKE + 2) == 1
     assert _chunk(lib, _desc(head_dim=256)) == 2
+    assert _chunk(lib, d, kv_len=(1 << 31) - 63) == 2
     # o_part is fp32: a row stride of 6 floats (24 bytes) is not 16-byte aligned.
     assert _chunk(lib, _desc(o_stride=S3(6, 6, 6)), kv_len=256) == 1
 

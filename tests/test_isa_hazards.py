@@ -1,0 +1,93 @@
+"""Hand-written matrix-core instructions keep their wait states in the build.
+
+Compiles each HIP source of the library to gfx950 assembly with the
+library's own flags and checks it with ``isa_hazards``.  The checker itself
+is pinned on small hand-made listings first, so that a checker that finds
+nothing cannot pass for a clean build.
+"""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from long_context_attention_attn_amd import build as libbuild
+
+from isa_hazards import check
+
+DEVICE_SOURCES = [s for s in libbuild.SOURCES if s.endswith(".hip")]
+
+
+def _listing(*body):
+    return "\n".join(["kern:"] + [f"\t{b}" for b in body] + ["\ts_endpgm"])
+
+
+ASM_MFMA = ";;#ASMSTART\n\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]\n\t;;#ASMEND"
+
+
+def test_checker_flags_a_move_right_before_an_asm_matrix_op():
+    text = _listing("v_mov_b64_e32 v[4:5], s[0:1]", "s_waitcnt lgkmcnt(0)", ASM_MFMA)
+    assert [h.kind for h in check(text)] == ["A"]
+    text = _listing("v_mov_b64_e32 v[4:5], s[0:1]", "s_nop 1", ASM_MFMA)
+    assert check(text) == []
+
+
+def test_checker_flags_an_early_read_of_an_asm_result():
+    text = _listing(ASM_MFMA, "s_nop 7", "v_accvgpr_read_b32 v9, a3")
+    assert [h.kind for h in check(text)] == ["B"]
+    text = _listing(ASM_MFMA, "s_nop 7", "s_nop 7", "s_nop 2", "v_accvgpr_read_b32 v9, a3")
+    assert check(text) == []
+    # Registers the matrix op does not write are free at once.
+    assert check(_listing(ASM_MFMA, "v_accvgpr_read_b32 v9, a16")) == []
+
+
+def test_checker_follows_branches_and_loop_back_edges():
+    # The read sits at the loop head; the matrix op at the bottom of the loop
+    # reaches it only through the back edge.
+    text = "\n".join([
+        "kern:",
+        ".LBB0_1:",
+        "\tv_accvgpr_read_b32 v9, a2",
+        "\ts_nop 7",
+        "\t" + ASM_MFMA,
+        "\ts_cbranch_scc1 .LBB0_1",
+        "\ts_endpgm",
+    ])
+    assert [h.kind for h in check(text)] == ["B"]
+    # A block entered only by a jump from elsewhere does not inherit the
+    # pending result of the code just above it.
+    text = "\n".join([
+        "kern:",
+        "\t" + ASM_MFMA,
+        "\ts_nop 7", "\ts_nop 7", "\ts_nop 7",
+        "\ts_branch .LBB0_3",
+        ".LBB0_2:",
+        "\tv_accvgpr_read_b32 v9, a2",
+        ".LBB0_3:",
+        "\ts_endpgm",
+    ])
+    assert check(text) == []
+
+
+def test_checker_leaves_compiler_matrix_ops_to_the_compiler():
+    text = _listing("v_mov_b64_e32 v[4:5], s[0:1]",
+                    "v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]")
+    assert check(text) == []
+
+
+@pytest.mark.parametrize("source", DEVICE_SOURCES)
+def test_built_kernels_keep_matrix_core_wait_states(source, tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    flags = [f for f in libbuild.HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    out = tmp_path / (source + ".s")
+    cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(libbuild.ROOT, "include"),
+           "-o", str(out), os.path.join(libbuild.CSRC, source)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    assert "v_mfma" in text or source == "lse_merge.hip"
+    hazards = check(text)
+    assert not hazards, "\n".join(str(h) for h in hazards[:20])
