@@ -1,46 +1,71 @@
 // Fused shifted-chunk attention forward, bf16 inputs, for gfx950 (CDNA4).
 //
-// A workgroup owns 256 query rows of one (batch, query head): eight waves of
-// 32 rows, two per SIMD.  It walks the KV chunks in the rank-shifted order
-// c_j = (j + rank) % J (the `shift` primitive of CommIR, papers.lqhl.me
-// summary "Mercury (SOSP 2025)", section 核心方法), 64 keys per tile, and
-// carries the online-softmax state in registers across chunk boundaries.
-// Rescaling that state when a chunk starts is exactly the log-sum-exp merge
-// of the chunk's partial result, so one launch computes what attn_chunk_fwd
-// followed by lse_merge computes chunk by chunk.  Chunk ranges that no query
-// of the workgroup can see (causal) are skipped without touching memory.
+// A workgroup owns 256 query rows of one (batch, query head): four waves, one
+// per SIMD, of 64 rows each (two 32-row query blocks).  It walks the KV
+// chunks in the rank-shifted order c_j = (j + rank) % J (the `shift`
+// primitive of CommIR, papers.lqhl.me summary "Mercury (SOSP 2025)", section
+// 核心方法), 64 keys per tile, and carries the online-softmax state in
+// registers across chunk boundaries.  Rescaling that state when a chunk
+// starts is exactly the log-sum-exp merge of the chunk's partial result, so
+// one launch computes what attn_chunk_fwd followed by lse_merge computes
+// chunk by chunk.  Chunk ranges that no query of the workgroup can see
+// (causal) are skipped without touching memory.
 //
-// Matrix cores (v_mfma_f32_32x32x16_bf16), per wave and 64-key tile:
+// Matrix cores (v_mfma_f32_32x32x16_bf16), per wave, query block qb and
+// 64-key tile:
 //   S^T[key][q] = sum_d K[key][d] Q[q][d]          2 key blocks x 8 steps
-//     A = K rows from LDS (ds_read_b128), B = Q^T resident in VGPRs.
+//     A = K rows from LDS (ds_read_b128), B = Q^T resident in registers.
 //   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]   4 d blocks x 4 steps
 //     A = V^T, read from row-major V in LDS with the transposing
 //         ds_read_b64_tr_b16, B = P^T taken straight from the S^T accumulator.
-// Each lane owns one query column of S^T, so the softmax row max/sum are
-// in-lane reductions plus one v_permlane32_swap with the lane holding the
-// other half of the keys.  Accumulator layout (lane l, register r):
-//   column = l % 32, row = 8*(r/4) + 4*(l/32) + (r%4).
+// A K operand read from LDS feeds both query blocks in key block 0 and one
+// of them in key block 1 (read twice there), a V operand feeds both: LDS
+// traffic per flop is well below that of 32-row waves, which is what bounds
+// the matrix cores when they are fed from LDS.
+// Each lane owns one query column of S^T per query block, so the softmax
+// row max/sum are in-lane reductions plus one v_permlane32_swap with the
+// lane holding the other half of the keys.  Accumulator layout (lane l,
+// register r): column = l % 32, row = 8*(r/4) + 4*(l/32) + (r%4).
 //
-// Ping-pong: waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise
-// and run the same loop one phase apart (group B starts one barrier late):
-//   MFMA phase j :  S = Q K[j]^T ;  O += P[j-1] V[j-1]
-//   barrier
-//   VALU phase j :  P[j] = softmax(S) ; A starts K[j+3], B starts V[j+3]
-//   barrier
-// so on every SIMD one wave feeds the matrix core while the other does the
-// exponentials.  K and V tiles stream straight from global memory into a
-// 4-deep LDS ring (global_load_lds_dwordx4, no registers involved), three
-// tiles ahead; each wave waits only for its own copies of the tile the next
-// barrier publishes.  A ring slot is refilled only after the phase that last
-// read it has passed a barrier.  Tiles sit in LDS unpadded with XOR-swizzled
-// 16-byte chunks (K: chunk ^ (row & 15); V: chunk ^ 4*(row & 3)) so that the
-// K reads and the transposing V reads are free of bank conflicts.
+// One wave per SIMD, so the overlap of matrix-core work and softmax work
+// comes from one instruction stream.  Tile j is processed in four quarters
+// of 16 matrix-core ops; each quarter also carries about a quarter of the
+// softmax work (exponentials of 16 scores per lane, partial row maxima):
+//   Q1: S[key block 0] of tile j      + exp of tile j-1, key block 1, qb 0
+//   Q2: S[key block 1] of tile j      + exp of tile j-1, key block 1, qb 1;
+//                                       max of tile j, key block 0
+//   Q3: O += P V, tile j-1, keys 0-31 + max of tile j, key block 1;
+//                                       exp of tile j, key block 0, qb 1
+//   Q4: O += P V, tile j-1, keys 32-63 + exp of tile j, key block 0, qb 0
+// The order is fixed with scheduling barriers at every step.
 //
-// Lazy rescaling: exponentials use a reference max m_ref that only moves
-// when a row's running max exceeds it by more than 8 (log2 units), so the
-// output accumulator is rescaled only on those rare tiles.  O and l share
-// the reference, so the result is unchanged; p <= 2^8 loses no relative
-// precision in fp32 or bf16.
+// K and V tiles stream straight from global memory into a 4-deep LDS ring
+// per tensor (global_load_lds_dwordx4, no registers involved): each wave
+// copies 16 rows of K tile j+3 and of V tile j+2 in Q1/Q2 (past the end of
+// the walk, the last tile again into a slot nothing reads, so every tile
+// issues the same copies), waits for its own copies of the tiles the next
+// tile needs, then all waves meet at one barrier per tile.  A slot is
+// refilled only after every read of its old tile has passed that barrier.
+// Tiles sit in LDS unpadded with XOR-swizzled 16-byte chunks (K: chunk ^
+// (row & 15); V: chunk ^ 4*(row & 3)) so that the K reads and the
+// transposing V reads are free of bank conflicts.
+//
+// Which tiles go where.  The hot loop (the main walk) takes, in visit order,
+// the full tiles that every query of the workgroup sees: no masking.  The
+// causal diagonal band and ragged ends (a few tiles per workgroup) follow in
+// a second loop, one tile at a time, masked.  Softmax partials merge the
+// same way in any order, so taking those tiles last changes only rounding.
+//
+// Reference max.  Exponentials use a per-row reference m_ref, set by the
+// first tile and left alone in the hot loop: O and the row sums stay
+// multiples of the same exp2(-m_ref), so nothing is ever rescaled there (O
+// is modified only by matrix-core ops inside the loop; any other write to
+// it makes the compiler keep extra copies of it).  A score more than 64
+// (log2 units) above the reference would let p exceed 2^64; real data does
+// not do that, but if a tile does, the wave raises a workgroup flag before
+// that tile's P V, every wave then feeds the tile's P to an all-zero V tile
+// and drops its sums, and the masked loop redoes the walk from that tile,
+// where the reference moves per tile with an explicit rescale of O and l.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -53,6 +78,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -60,131 +86,176 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kBlockMBf16;  // 256 query rows per workgroup
 constexpr int kN = 64;                // keys per tile
 constexpr int kTile = kN * 128;       // elements of one K or V tile (16 KB, unpadded)
+constexpr int kTileBytes = kTile * 2;
 constexpr int kRing = 4;              // LDS ring depth per stream
-constexpr float kRescaleSlack = 8.0f;  // log2 units
-static_assert(kBlockM == kWaves * 32, "32 query rows per wave");
+// The reference max of a row moves (which needs the accumulated O and l
+// rescaled) only when a score exceeds it by more than this, in log2 units.
+// Until then p <= 2^64: with |v| < 2^40 and < 2^31 keys, O and l stay far
+// below the fp32 range, and fp32 / bf16 keep full relative precision.
+constexpr float kRescaleSlack = 64.0f;
+static_assert(kBlockM == kWaves * 64, "64 query rows per wave");
 
-struct TileWalk {
-  int j;       // step in visit order
-  int64_t hi;  // end of the current chunk segment (global position)
-  int64_t t0;  // tile start (global position)
+// The tiles a workgroup visits.  Chunk c covers key rows [c*C, (c+1)*C) of
+// the buffer; visiting chunks in the order (j + rank) % J walks rows
+// [rank*C, J*C) and then [0, rank*C).  With the causal limit (one past the
+// workgroup's last query position, relative to row 0) that is two
+// contiguous ranges, each cut into 64-row tiles from its start.  Tile
+// boundaries need not fall on chunk boundaries: the keys are taken in
+// exactly the visit order either way.
+struct Walk {
+  int a0, a_end, b0, b_end, n_a, n;
 };
 
-__device__ __forceinline__ bool segment(const FwdParams& p, int j, int64_t limit, int64_t& lo,
-                                        int64_t& hi) {
-  int c = (j + p.rank) % p.num_chunks;
-  lo = p.kv_pos0 + (int64_t)c * p.chunk_len;
-  hi = lo + p.chunk_len;
-  if (hi > limit) hi = limit;
-  return hi > lo;
+__device__ __forceinline__ Walk make_walk(int a0, int a_end, int b0, int b_end) {
+  Walk w;
+  w.a0 = a0;
+  w.a_end = a_end;
+  w.b0 = b0;
+  w.b_end = b_end;
+  w.n_a = a_end > a0 ? (a_end - a0 + kN - 1) / kN : 0;
+  w.n = w.n_a + (b_end > b0 ? (b_end - b0 + kN - 1) / kN : 0);
+  return w;
 }
 
-__device__ __forceinline__ bool walk_from(const FwdParams& p, int j0, int64_t limit, TileWalk& w) {
-  for (int j = j0; j < p.num_chunks; ++j) {
-    int64_t lo, hi;
-    if (segment(p, j, limit, lo, hi)) {
-      w.j = j;
-      w.hi = hi;
-      w.t0 = lo;
-      return true;
-    }
+// Start row and end row (exclusive) of tile `it` of the walk.
+__device__ __forceinline__ void tile_bounds(const Walk& w, int it, int& t0, int& t_end) {
+  if (it < w.n_a) {
+    t0 = w.a0 + kN * it;
+    t_end = min(t0 + kN, w.a_end);
+  } else {
+    t0 = w.b0 + kN * (it - w.n_a);
+    t_end = min(t0 + kN, w.b_end);
   }
-  return false;
 }
-
-__device__ __forceinline__ bool walk_next(const FwdParams& p, int64_t limit, TileWalk& w) {
-  if (w.t0 + kN < w.hi) {
-    w.t0 += kN;
-    return true;
-  }
-  return walk_from(p, w.j + 1, limit, w);
-}
-
-__device__ __forceinline__ int tile_rows(const TileWalk& w) { return (int)min((int64_t)kN, w.hi - w.t0); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Waits until at most n (0, 4 or 8) of this wave's global->LDS copies are
-// still in flight.
+// Waits until at most n (a multiple of 4 in [0, 16]) of this wave's
+// global->LDS copies are still in flight.
 __device__ __forceinline__ void wait_copies(int n) {
-  if (n == 0)
-    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
-  else if (n == 4)
-    __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4)
-  else
-    __builtin_amdgcn_s_waitcnt(0xF78);  // vmcnt(8)
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;   // vmcnt(0)
+    case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;   // vmcnt(4)
+    case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;   // vmcnt(8)
+    case 12: __builtin_amdgcn_s_waitcnt(0xF7C); break;  // vmcnt(12)
+    default: __builtin_amdgcn_s_waitcnt(0x4F70); break; // vmcnt(16)
+  }
 }
 
 // Workgroup barrier without the release fence __syncthreads() adds: that
 // fence would wait for every global->LDS copy in flight, including the
 // prefetches of later tiles.  Copies a barrier must publish are waited for
 // explicitly with wait_copies(); LDS reads before a barrier have all returned
-// (their data fed matrix-core ops of the phase).
-__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// (their data fed matrix-core ops).
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Global -> LDS copy of one 64-row tile of K or V by the four waves of a wave
-// group.  Wave wg copies rows 16*wg .. 16*wg+15 with four 1 KB instructions;
-// lane i of instruction n writes LDS chunk i of rows 16*wg + 4*n + i/16,
-// i.e. physical 16-byte chunk i%16 of that row, which holds logical chunk
-// (i%16) ^ swz(row).  Rows past the tile end copy its last row instead (in
-// bounds; their keys are masked and their P is 0).
-struct CopyLane {
-  int row[4];  // tile row of instruction n
-  int col[4];  // element offset of the logical chunk within the row
+// Global -> LDS copy of one 64-row tile of K or V by the four waves.  Wave w
+// copies rows 16*w .. 16*w+15 with four 1 KB instructions; lane i of
+// instruction n writes LDS chunk i of rows 16*w + 4*n + i/16, i.e. physical
+// 16-byte chunk i%16 of that row, which holds logical chunk (i%16) ^ swz(row).
+// The source address is a wave-uniform base in SGPRs plus a per-lane 32-bit
+// byte offset.  K (swz = row & 15) keeps one offset per instruction; for V
+// (swz = 4*(row & 3) = 4*(i/16)) the offset is the same for all four and the
+// row step goes into the base.  In a ragged tile, rows past its end copy its
+// last row instead (in bounds; their keys are masked and their P is 0).
+struct CopyLanes {
+  uint32_t k_off[4];  // K: byte offset of instruction n's source in a full tile
+  uint32_t v_off;     // V: byte offset within 4 rows, same for every n
 };
 
-__device__ __forceinline__ void copy_lane_init(CopyLane& cl, bool v_layout, int wg, int lane) {
+__device__ __forceinline__ uint32_t k_chunk(int row, int lane) {
+  return (uint32_t)((lane & 15) ^ (row & 15)) * 16u;
+}
+__device__ __forceinline__ uint32_t v_chunk(int row, int lane) {
+  return (uint32_t)((lane & 15) ^ (4 * (row & 3))) * 16u;
+}
+
+__device__ __forceinline__ void copy_lanes_init(CopyLanes& cl, int w, int lane, uint32_t k_stride_b,
+                                                uint32_t v_stride_b) {
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
-    const int row = 16 * wg + 4 * n + (lane >> 4);
-    const int pc = lane & 15;
-    const int lc = v_layout ? (pc ^ (4 * (row & 3))) : (pc ^ (row & 15));
-    cl.row[n] = row;
-    cl.col[n] = lc * 8;
+    const int row = 16 * w + 4 * n + (lane >> 4);
+    cl.k_off[n] = (uint32_t)row * k_stride_b + k_chunk(row, lane);
   }
+  const int row0 = 16 * w + (lane >> 4);
+  cl.v_off = (uint32_t)row0 * v_stride_b + v_chunk(row0, lane);
 }
 
-// The copy is written as inline assembly on purpose: through the builtin,
-// the compiler cannot tell which LDS bytes a copy writes and makes every
-// later LDS read wait for all copies in flight, prefetches included.  Here
-// every wait is explicit (wait_copies before the barrier that publishes a
-// tile).  M0 holds the LDS destination; one wait state must separate its
-// scalar write from the copy that reads it.
-__device__ __forceinline__ void copy_tile(__bf16* lds_tile, const __bf16* gtile, int rows,
-                                          int stride, const CopyLane& cl, int wg) {
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int r = min(cl.row[n], rows - 1);
-    const __bf16* src = gtile + (r * stride + cl.col[n]);
-    const uint32_t lds_addr =
-        (uint32_t)(uintptr_t)(lds_void*)(lds_tile + (16 * wg + 4 * n) * 128);
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(lds_addr), "v"(src)
-        : "memory", "m0");
+// One 1 KB copy instruction.  Written as inline assembly on purpose: through
+// the builtin, the compiler cannot tell which LDS bytes a copy writes and
+// makes every later LDS read wait for all copies in flight, prefetches
+// included.  Here every wait is explicit (wait_copies before the barrier
+// that publishes a tile).  M0 holds the LDS destination; one wait state must
+// separate its scalar write from the copy that reads it.  Nothing else in
+// the kernel uses M0.
+__device__ __forceinline__ void copy_one(uint32_t lds_addr, const __bf16* gbase, uint32_t off) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(off), "s"(gbase)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// One tile copy of this wave: LDS byte address of the wave's first row in the
+// slot, global address of tile row 0, valid rows, row stride.
+struct TileCopy {
+  uint32_t dst;
+  const __bf16* src;
+  int rows;
+  uint32_t stride_b;
+};
+
+// Instruction n (0..3) of a K tile copy.
+__device__ __forceinline__ void copy_k(const TileCopy& tc, const CopyLanes& cl, int n, int w,
+                                       int lane) {
+  uint32_t off = cl.k_off[n];
+  if (tc.rows < kN) {  // rare: ragged tile
+    const int row = 16 * w + 4 * n + (lane >> 4);
+    const int r = min(row, tc.rows - 1);
+    off = (uint32_t)r * tc.stride_b + k_chunk(row, lane);
   }
+  copy_one(tc.dst + 1024u * n, tc.src, off);
 }
 
-// Step t of S (key block t/8, d step t%8): this lane's row is kb*32 + lq, its
-// logical chunk 2*(t%8) + hh, physical chunk logical ^ (lq & 15).  koff[kk]
-// is the byte offset for key block 0; key block 1 is 32 rows (8 KB) further.
-__device__ __forceinline__ bf16x8 read_k(const __bf16* ktile, const int (&koff)[8], int t) {
-  return *(const bf16x8*)((const char*)ktile + koff[t & 7] + (t >> 3) * 8192);
+// Instruction n (0..3) of a V tile copy.
+__device__ __forceinline__ void copy_v(const TileCopy& tc, const CopyLanes& cl, int n, int w,
+                                       int lane) {
+  uint32_t off = cl.v_off;
+  const __bf16* base = tc.src + (size_t)(4 * n) * (tc.stride_b >> 1);
+  if (tc.rows < kN) {  // rare: ragged tile
+    const int row = 16 * w + 4 * n + (lane >> 4);
+    const int r = min(row, tc.rows - 1);
+    off = (uint32_t)r * tc.stride_b + v_chunk(row, lane);
+    base = tc.src;
+  }
+  copy_one(tc.dst + 1024u * n, base, off);
 }
 
-// Step t of P V (16-key step t/4, d block t%4): two transposing reads 8 rows
-// apart.  voff[db] is this lane's byte address for 16-key step 0; step ks is
-// 16 rows (4 KB) further.
-__device__ __forceinline__ bf16x8 read_v(const __bf16* vtile, const int (&voff)[4], int t) {
-  const char* src = (const char*)vtile + voff[t & 3] + (t >> 2) * 4096;
+// K operand of step kk of key block kb: this lane's row is kb*32 + lq, its
+// logical chunk 2*kk + hh, physical chunk logical ^ (lq & 15).  koff[kk] is
+// the byte offset for key block 0; key block 1 is 32 rows (8 KB) further.
+__device__ __forceinline__ bf16x8 read_k(const __bf16* ktile, const int (&koff)[8], int kb,
+                                         int kk) {
+  return *(const bf16x8*)((const char*)ktile + koff[kk] + kb * 8192);
+}
+
+// V^T operand of 16-key step ks, d block db: two transposing reads 8 rows
+// apart.  voff[db] is this lane's byte address for step 0; step ks is 16
+// rows (4 KB) further.
+__device__ __forceinline__ bf16x8 read_v(const __bf16* vtile, const int (&voff)[4], int ks,
+                                         int db) {
+  const char* src = (const char*)vtile + voff[db] + ks * 4096;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 2048));
   bf16x8 a;
@@ -193,83 +264,62 @@ __device__ __forceinline__ bf16x8 read_v(const __bf16* vtile, const int (&voff)[
   return a;
 }
 
-// One MFMA phase of the wave:
-//  * S^T (2 key blocks) of its 32 queries against K tile `ktile`;
-//  * the second half of the previous tile's softmax: s_hi holds that tile's
-//    scores for key block 1; p = exp2(s*c - m_use) goes to pb[2], pb[3] and
-//    its sum is returned;
-//  * O^T += V^T P^T for the previous tile (V tile `vtile`).
-// The first 8 S steps are each paired with one P V step of key block 0 (its
-// P is ready) and two exponentials; the P V steps of key block 1 follow the
-// last 8 S steps.  Operand reads run 4 steps ahead.  The order is fixed with
-// scheduling barriers so the compiler neither serialises reads and
-// matrix-core ops nor hoists every read.
-__device__ __forceinline__ float mfma_phase(const __bf16* ktile, const __bf16* vtile,
-                                            const int (&koff)[8], const int (&voff)[4],
-                                            const bf16x8 (&qv)[8], bf16x8 (&pb)[4],
-                                            const f32x16& s_hi, float c, float m_use,
-                                            f32x16 (&s)[2], f32x16 (&o)[4]) {
-  constexpr int kAhead = 4;
-  bf16x8 ka[kAhead], va[kAhead];
-#pragma unroll
-  for (int t = 0; t < kAhead; ++t) {
-    ka[t] = read_k(ktile, koff, t);
-    va[t] = read_v(vtile, voff, t);
-  }
-  s[0] = (f32x16){};
-  s[1] = (f32x16){};
-  float rs[2] = {0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    __builtin_amdgcn_sched_barrier(0);
-    s[t >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % kAhead], qv[t & 7], s[t >> 3], 0,
-                                                        0, 0);
-    if (t < 8) {
-      o[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % kAhead], pb[t >> 2], o[t & 3], 0,
-                                                         0, 0);
-      // Two exponentials of the previous tile's key block 1 per step, all
-      // done before the new key block 1 (step 8 on) reuses those registers.
-      const float e0 = exp2_fast(fmaf(s_hi[2 * t], c, -m_use));
-      const float e1 = exp2_fast(fmaf(s_hi[2 * t + 1], c, -m_use));
-      rs[0] += e0;
-      rs[1] += e1;
-      pb[2 + (t >> 2)][(2 * t) & 7] = (__bf16)e0;
-      pb[2 + (t >> 2)][(2 * t + 1) & 7] = (__bf16)e1;
-    }
-    if (t + kAhead < 16) ka[t % kAhead] = read_k(ktile, koff, t + kAhead);
-    if (t < 8 && t + kAhead < 16) va[t % kAhead] = read_v(vtile, voff, t + kAhead);
-  }
-#pragma unroll
-  for (int u = 8; u < 16; ++u) {
-    __builtin_amdgcn_sched_barrier(0);
-    o[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[u % kAhead], pb[u >> 2], o[u & 3], 0, 0,
-                                                       0);
-    if (u + kAhead < 16) va[u % kAhead] = read_v(vtile, voff, u + kAhead);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  return rs[0] + rs[1];
+// S^T += K Q^T for one 16-deep d step, Q^T taken from AGPRs (qk_mfma0: the
+// first step, accumulator starting at zero).  All matrix-core ops are
+// written as assembly: the compiler otherwise places every accumulator in
+// AGPRs (scores included, which the softmax then has to copy out) and keeps
+// Q^T in VGPRs.  Hazards are handled by construction: an accumulator is
+// read only by the next op on it or, by vector ALU code, at least eight
+// matrix-core ops later; the few places that read sooner call
+// matrix_settle() first.
+__device__ __forceinline__ void qk_mfma(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void qk_mfma0(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
 }
 
-// The second half of a tile's softmax alone (after the loop).
-__device__ __forceinline__ float softmax_hi(bf16x8 (&pb)[4], const f32x16& s_hi, float c,
-                                            float m_use) {
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const float e = exp2_fast(fmaf(s_hi[t], c, -m_use));
-    rs[t & 3] += e;
-    pb[2 + (t >> 3)][t & 7] = (__bf16)e;
-  }
-  return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+// O^T += V^T P^T with the accumulator in AGPRs: O is touched only by these
+// ops inside the loop.  P is written by vector ALU code a quarter tile
+// before the op that reads it; V comes from an LDS read the compiler waits
+// for.
+__device__ __forceinline__ void pv_mfma(f32x16& o, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
-// O^T += V^T P^T alone (the last tile, after the loop).
-__device__ __forceinline__ void pv_tile(const __bf16* vtile, const int (&voff)[4],
-                                        const bf16x8 (&pb)[4], f32x16 (&o)[4]) {
-#pragma unroll
-  for (int t = 0; t < 16; ++t)
-    o[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vtile, voff, t), pb[t >> 2], o[t & 3],
-                                                       0, 0, 0);
+// O and Q^T live in AGPRs.  Reading or rescaling O goes through a VGPR
+// copy made by these empty statements, so that O itself is never used by a
+// vector ALU instruction: otherwise the compiler keeps O in VGPRs and copies
+// it into AGPRs around every O^T op.
+template <typename T>
+__device__ __forceinline__ T agpr_get(const T& o) {
+  T t;
+  asm volatile("" : "=v"(t) : "0"(o));
+  return t;
+}
+template <typename T>
+__device__ __forceinline__ void agpr_set(T& o, const T& t) {
+  asm volatile("" : "=a"(o) : "0"(t));
+}
+
+// Wait states between a matrix-core op and another instruction that reads
+// or writes its result (a 32x32x16 op runs 16 passes).
+__device__ __forceinline__ void matrix_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// Two probabilities p = exp2(s*c - m) of scores s[r], s[r+1], rounded to
+// bf16 into P operand slots x, x+1 of `dst`; their fp32 values are added to
+// `acc`.  (Summing the bf16 values instead would leave rows with few keys
+// with a relative error of up to 2^-9 in the sum, i.e. in the LSE.)
+__device__ __forceinline__ void exp_pair(const f32x16& s, int r, float c, float m, bf16x8& dst,
+                                         int x, float& acc) {
+  const float e0 = exp2_fast(fmaf(s[r], c, -m));
+  const float e1 = exp2_fast(fmaf(s[r + 1], c, -m));
+  dst[x] = (__bf16)e0;
+  dst[x + 1] = (__bf16)e1;
+  acc += e0 + e1;
+  asm volatile("" : "+v"(acc));
 }
 
 // NaN-propagating maximum (v_maximum3_f32 on gfx950; unlike fmaxf it needs
@@ -302,21 +352,18 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const f32x4& v) {
 
 // Keys of a tile that a query cannot see become -inf: keys at or past t_end,
 // and (causal) keys after the query's global position.  rel0 = (global
-// position of the wave's first query) - t0, a wave-uniform value; the lane's
-// query is rel0 + lq positions past the tile start.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], bool causal, int64_t rel0, int64_t t0,
-                                          int64_t t_end, int lq, int hh) {
-  // Clamp the wave-uniform parts to small ints before adding the lane part.
-  const int last = (int)(t_end - 1 - t0);  // in [0, kN)
-  const int rel = causal ? (int)max(min(rel0, (int64_t)kN), (int64_t)-64) : kN;
+// position of the block's first query) - t0, a wave-uniform value; the
+// lane's query is rel0 + lq positions past the tile start.
+__device__ __forceinline__ void mask_block(f32x16& s0, f32x16& s1, bool causal, int rel0,
+                                           int last, int lq, int hh) {
+  const int rel = causal ? max(min(rel0, kN), -kN) : kN;
   const int lim = min(rel + (causal ? lq : 0), last) - 4 * hh;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int koff = kb * 32 + 8 * (r >> 2) + (r & 3);
-      s[kb][r] = koff <= lim ? s[kb][r] : -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int koff = 8 * (r >> 2) + (r & 3);
+    s0[r] = koff <= lim ? s0[r] : -INFINITY;
+    s1[r] = koff + 32 <= lim ? s1[r] : -INFINITY;
+  }
 }
 
 // Makes the compiler wait for outstanding loads into v before going on.
@@ -326,21 +373,22 @@ __device__ __forceinline__ void settle(const T& v) {
 }
 
 template <typename TOut>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[kRing][kTile];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[kRing][kTile];
-  // All zeros: the V tile P V reads when P is known to be zero (a dead
-  // tile), so that non-finite values in a V tile no query of the wave can
-  // see never reach it through 0 * NaN.
+  // All zeros: the V tile P V reads when every query of the wave is past
+  // the tile (P known to be zero), so that non-finite values in a V tile no
+  // query of the wave can see never reach it through 0 * NaN.
   __shared__ __attribute__((aligned(16))) __bf16 lds_vzero[kTile];
+  // Set by a wave whose scores outgrow the reference: all waves start over.
+  __shared__ int lds_flag;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in [0, 8)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in [0, 4)
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int hh = lane >> 5;
-  const bool group_b = wave >= 4;
-  const int wg = wave & 3;  // wave index within its group
 
   // Block -> work item.  The hardware deals consecutive blocks round-robin to
   // the 8 XCDs; remap so that the work items sharing one KV head land on one
@@ -360,27 +408,84 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 
   const int64_t q_start = (int64_t)qt * kBlockM;
   const int64_t q_rows_wg = min((int64_t)kBlockM, p.seq_q - q_start);
-  const int64_t wave_q0 = q_start + wave * 32;
-  const int64_t limit = p.causal ? p.q_pos0 + q_start + q_rows_wg : INT64_MAX;
-  const int64_t wave_qpos_min = p.q_pos0 + wave_q0;
-  // Last query position of the wave (below wave_qpos_min if it has no rows).
-  const int64_t wave_qpos_max = p.q_pos0 + min(wave_q0 + 31, p.seq_q - 1);
+  const int64_t wave_q0 = q_start + wave * 64;
+  // Query positions relative to key row 0, clamped to [-1, kv_rows]: -1 sees
+  // no key, kv_rows sees every key.
+  const int kv_rows = p.kv_rows;
+  auto rel = [&](int64_t q_index) {
+    return (int)max((int64_t)-1, min(p.q_rel0 + q_index, (int64_t)kv_rows));
+  };
+  // The same for the first query of a 32-row block, clamped no higher than
+  // -kN below, so that adding the row index keeps every row's own limit
+  // exact (a row left of key 0 stays left of it).
+  auto rel_block = [&](int64_t q_index) {
+    return (int)max((int64_t)-kN, min(p.q_rel0 + q_index, (int64_t)kv_rows));
+  };
+  // One past the last key any query of the workgroup can see, and one past
+  // the last key every query of it sees.
+  const int limit = p.causal ? rel(q_start + q_rows_wg - 1) + 1 : kv_rows;
+  const int ulim = p.causal ? rel(q_start) + 1 : kv_rows;
+  // The main walk takes the full tiles every query sees, in visit order; the
+  // rest (the causal diagonal band, ragged ends: at most a few tiles) comes
+  // after it, with masking.  The softmax merge does not depend on the order.
+  const int a0 = p.seg_a0;
+  const int a_lim = min(kv_rows, limit);
+  const int b_lim = min(a0, limit);
+  const int a_main = a0 + kN * (max(0, min(a_lim, ulim) - a0) / kN);
+  const int b_main = kN * (max(0, min(b_lim, ulim)) / kN);
+  const Walk walk = make_walk(a0, a_main, 0, b_main);
+  const Walk rest_walk = make_walk(a_main, a_lim, b_main, b_lim);
+  const int n_tiles = walk.n;
+  const int wave_q_min = rel(wave_q0);
+  // Last query of the wave (below wave_q_min if the wave has no rows).
+  const int wave_q_max = rel(min(wave_q0 + 63, p.seq_q - 1));
 
   const __bf16* qbase = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
   const __bf16* kbase = (const __bf16*)p.k + b * p.k_sb + hk * p.k_sh;
   const __bf16* vbase = (const __bf16*)p.v + b * p.v_sb + hk * p.v_sh;
-  // Group A streams K tiles, group B streams V tiles.
-  const __bf16* my_base = group_b ? vbase : kbase;
-  const int my_stride = (int)(group_b ? p.v_ss : p.k_ss);
-  __bf16* const my_ring = group_b ? &lds_v[0][0] : &lds_k[0][0];
-  auto tile_ptr = [&](int64_t t0) { return my_base + (t0 - p.kv_pos0) * my_stride; };
-  CopyLane cl;
-  copy_lane_init(cl, group_b, wg, lane);
+  // The sequence strides are below 2^24 elements (checked on the host), so a
+  // tile spans < 2^31 bytes.
+  const uint32_t k_stride_b = (uint32_t)p.k_ss * 2u;
+  const uint32_t v_stride_b = (uint32_t)p.v_ss * 2u;
+  // LDS byte address of this wave's first row in ring slot 0.
+  const uint32_t k_ring = lds_address(&lds_k[0][0]) + (uint32_t)(16 * wave) * 256u;
+  const uint32_t v_ring = lds_address(&lds_v[0][0]) + (uint32_t)(16 * wave) * 256u;
+  CopyLanes cl;
+  copy_lanes_init(cl, wave, lane, k_stride_b, v_stride_b);
+  auto k_copy = [&](const Walk& wk, int it, int slot) {
+    TileCopy tc;
+    int t0, te;
+    tile_bounds(wk, it, t0, te);
+    tc.dst = k_ring + (uint32_t)slot * kTileBytes;
+    tc.src = kbase + (int64_t)t0 * p.k_ss;
+    tc.rows = te - t0;
+    tc.stride_b = k_stride_b;
+    return tc;
+  };
+  auto v_copy = [&](const Walk& wk, int it, int slot) {
+    TileCopy tc;
+    int t0, te;
+    tile_bounds(wk, it, t0, te);
+    tc.dst = v_ring + (uint32_t)slot * kTileBytes;
+    tc.src = vbase + (int64_t)t0 * p.v_ss;
+    tc.rows = te - t0;
+    tc.stride_b = v_stride_b;
+    return tc;
+  };
+  auto copy_tile_k = [&](const TileCopy& tc) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) copy_k(tc, cl, n, wave, lane);
+  };
+  auto copy_tile_v = [&](const TileCopy& tc) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) copy_v(tc, cl, n, wave, lane);
+  };
 
-  // Q^T operand, resident for the whole kernel.
-  bf16x8 qv[8];
-  {
-    const int64_t my_q = wave_q0 + lq;
+  // Q^T operands of both query blocks, resident in AGPRs for the whole kernel.
+  bf16x8 qv[2][8];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t my_q = wave_q0 + 32 * qb + lq;
     const bool row_ok = my_q < p.seq_q;
     const int64_t row = row_ok ? my_q : 0;
 #pragma unroll
@@ -391,10 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
       y[1] = row_ok ? x[1] : 0u;
       y[2] = row_ok ? x[2] : 0u;
       y[3] = row_ok ? x[3] : 0u;
-      qv[kk] = __builtin_bit_cast(bf16x8, y);
+      agpr_set(qv[qb][kk], __builtin_bit_cast(bf16x8, y));
     }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) settle(qv[kk]);
   }
 
   // Per-lane LDS byte offsets of the matrix-core operands (see read_k, read_v).
@@ -409,182 +512,347 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
       voff[db] = row * 256 + (((db * 4 + 2 * gq + (u >> 1)) ^ (4 * t)) * 16) + (u & 1) * 8;
   }
 
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
-  float m_ref = -INFINITY;
-  float l_run = 0.f;
   const float c = p.scale_log2;
-  bf16x8 pb[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int x = 0; x < 8; ++x) pb[ks][x] = (__bf16)0.f;
-
-  // Tiles j (current) .. j+3 of the visit order.
-  TileWalk t_cur, t_n1, t_n2, t_n3;
-  bool have = walk_from(p, 0, limit, t_cur);
-  t_n1 = t_cur;
-  bool have1 = have && walk_next(p, limit, t_n1);
-  t_n2 = t_n1;
-  bool have2 = have1 && walk_next(p, limit, t_n2);
-
-  // Prologue: the zero V tile, and tiles 0..2 of each group's stream.
   {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int i = tid; i < kTile / 8; i += kThreads) *(u32x4*)(lds_vzero + 8 * i) = zero;
   }
-  if (have) copy_tile(my_ring, tile_ptr(t_cur.t0), tile_rows(t_cur), my_stride, cl, wg);
-  if (have1) copy_tile(my_ring + kTile, tile_ptr(t_n1.t0), tile_rows(t_n1), my_stride, cl, wg);
-  if (have2) copy_tile(my_ring + 2 * kTile, tile_ptr(t_n2.t0), tile_rows(t_n2), my_stride, cl, wg);
+  f32x16 o[2][4];
+  float m_ref[2], m_use[2];  // reference max; m_use = m_ref, or 0 while it is -inf
+  float l_run[2];            // this lane's half of the row sums
+  // P^T operands: pb[qb][ks] holds keys 16*ks .. 16*ks+15 of the tile being
+  // multiplied into O (ks 0-1: key block 0, ks 2-3: key block 1).
+  bf16x8 pb[2][4];
+  // Scores of the current tile; s[1][*] of tile j-1 lives on into Q1/Q2 of
+  // tile j, which take its exponentials.
+  f32x16 s[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], (f32x16){});
+    m_ref[qb] = -INFINITY;
+    m_use[qb] = 0.f;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) pb[qb][ks][x] = (__bf16)0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][qb][r] = -INFINITY;
+  }
+  if (tid == 0) __atomic_store_n(&lds_flag, 0, __ATOMIC_RELAXED);
+  // The compiler must not know P's starting value: a known constant gets
+  // rebuilt by vector moves right in front of the asm matrix ops, which do
+  // not see the wait states such a move needs before a matrix-core read.
+  asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[0][2]), "+v"(pb[0][3]),
+               "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pb[1][2]), "+v"(pb[1][3]));
+
+  // ---- Main walk.  The first tile sets each row's reference (nothing is
+  // accumulated yet).  A later score more than the slack above it (which
+  // real data does not produce) stops the walk for all waves before that
+  // tile's P V; the rest loop below then takes over from that tile.
+  if (n_tiles > 0) {
+    copy_tile_k(k_copy(walk, 0, 0));
+    copy_tile_v(v_copy(walk, 0, 0));
+  }
+  if (n_tiles > 1) {
+    copy_tile_k(k_copy(walk, 1, 1));
+    copy_tile_v(v_copy(walk, 1, 1));
+  }
+  if (n_tiles > 2) copy_tile_k(k_copy(walk, 2, 2));
   wait_copies(0);
   __syncthreads();
-  if (group_b) phase_barrier();  // group B runs one phase behind group A
 
-  int slot = 0;            // ring slot of tile j
-  bool dead_prev = true;   // P[j-1] is all zeros (no tile before the first)
-  // Second half of the previous tile's softmax, finished in the next MFMA
-  // phase: its key-block-1 scores and the reference they are taken against.
-  f32x16 s_hi;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s_hi[r] = -INFINITY;
-  float m_use = 0.f;
-  // The hot loop below modifies O only through the matrix-core ops: a tile
-  // whose scores would move the reference max leaves it, and the outer loop
-  // rescales O and finishes that tile.  (Rescaling inside the loop makes the
-  // compiler keep two register copies of O and move all 64 values between
-  // them twice per tile.)
-  f32x16 s[2];
-  int64_t t0 = 0, t_end = 0;
-  bool dead = true, have3 = false;
-  float m_tile = -INFINITY;
+  int slot = 0;
+  bool dead_prev = true;  // P[j-1] is all zeros (before the first tile)
+  float rs_pend[2] = {0.f, 0.f};  // key-block-0 sums of tile j-1
+  int it = 0;
+  int stopped_at = n_tiles;  // iteration whose start saw a request to stop
+  for (; it < n_tiles; ++it) {
+    // This tile copies K tile j+3 and V tile j+2 (main-walk tiles are full:
+    // no row clamping).  Past the end of the walk the last tile is copied
+    // again, into a ring slot no later read uses.
+    const int kt = min(it + 3, n_tiles - 1), vt = min(it + 2, n_tiles - 1);
+    const __bf16* ksrc =
+        kbase + (int64_t)(kt < walk.n_a ? walk.a0 + kN * kt : kN * (kt - walk.n_a)) * p.k_ss;
+    const __bf16* vsrc =
+        vbase + (int64_t)(vt < walk.n_a ? walk.a0 + kN * vt : kN * (vt - walk.n_a)) * p.v_ss;
+    const uint32_t kdst = k_ring + (uint32_t)((slot + 3) & (kRing - 1)) * kTileBytes;
+    const uint32_t vdst = v_ring + (uint32_t)((slot + 2) & (kRing - 1)) * kTileBytes;
+    const __bf16* ktile = &lds_k[slot][0];
+    // Set by a wave at tile j-1 (before the last barrier): tile j-1's P V
+    // then reads the zero tile, its sums are dropped, and the walk stops
+    // after this tile; the rest loop redoes it from tile j-1.
+    const bool flag = __builtin_amdgcn_readfirstlane(
+                          __atomic_load_n(&lds_flag, __ATOMIC_RELAXED)) != 0;
+    const __bf16* vtile =
+        (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
+    float rh[2] = {0.f, 0.f};  // sums of tile j-1, key block 1
+    float mx[2] = {-INFINITY, -INFINITY};
 
-  // Second part of the VALU phase: exponentials of key block 0 (or P = 0
-  // for a dead tile), the copy of tile j+3, the wait for tile j+1, the
-  // barrier, and the rotation of the tile window.
-  auto valu_rest = [&]() __attribute__((always_inline)) {
-    if (dead) {
+    // ---- Q1, Q2: S of tile j.  Step t < 8: key block 0, d step t, both
+    // query blocks; 8 <= t < 16: key block 1 for qb 0; t >= 16: key block 1
+    // for qb 1 (its K operands read again, so that the old scores of qb 1
+    // are consumed before they are overwritten).  Alongside: exp of tile
+    // j-1, key block 1 (qb 0 in t < 8, qb 1 in 8 <= t < 16), copies of K
+    // tile j+3 and V tile j+2, and the max of key block 0 (t >= 16).
+    bf16x8 ka[3];
+    ka[0] = read_k(ktile, koff, 0, 0);
+    ka[1] = read_k(ktile, koff, 0, 1);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) pb[ks][x] = (__bf16)0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_hi[r] = -INFINITY;
-      m_use = 0.f;
-    } else {
-      m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      // First half (key block 0) now; key block 1 in the next MFMA phase.
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2_fast(fmaf(s[0][r], c, -m_use));
-        rs[r & 3] += e;
-        pb[r >> 3][r & 7] = (__bf16)e;
+    for (int t = 0; t < 24; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int kk = t & 7;
+      if (t + 2 < 24) {
+        const int u = t + 2;
+        ka[u % 3] = read_k(ktile, koff, u >= 8 ? 1 : 0, u & 7);
       }
-      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-      s_hi = s[1];
-    }
-    dead_prev = dead;
-
-    // Stream: start tile j+3 of this group's stream into the slot that held
-    // tile j-1 (last read before the previous barrier), then wait until tile
-    // j+1 of the stream has fully landed: only copies of tiles j+2 and j+3
-    // (issued after it) may still be in flight.
-    if (have3)
-      copy_tile(my_ring + ((slot + 3) & (kRing - 1)) * kTile, tile_ptr(t_n3.t0), tile_rows(t_n3),
-                my_stride, cl, wg);
-    wait_copies(4 * ((int)have2 + (int)have3));
-    // Finish this phase's softmax work before the barrier: without this the
-    // compiler sinks the exponentials into the next matrix-core phase.
-    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(s_hi), "v"(l_run) : "memory");
-    phase_barrier();
-
-    t_cur = t_n1;
-    have = have1;
-    t_n1 = t_n2;
-    have1 = have2;
-    t_n2 = t_n3;
-    have2 = have3;
-    slot = (slot + 1) & (kRing - 1);
-  };
-
-  while (have) {
-    bool move_ref = false;
-    do {
-      t0 = t_cur.t0;
-      t_end = min(t0 + kN, t_cur.hi);
-      t_n3 = t_n2;
-      have3 = have2 && walk_next(p, limit, t_n3);
-      // A tile is dead for this wave when every key of it lies after every
-      // query of the wave (causal) or the wave holds no query rows: its
-      // softmax is skipped, P = 0, and its P V reads the zero tile.  (The
-      // matrix-core ops still run: a branch around them costs more in
-      // register copies than it saves.)
-      dead = (p.causal && t0 > wave_qpos_max) || wave_q0 >= p.seq_q;
-
-      // ---- MFMA phase ------------------------------------------------------
-      __builtin_amdgcn_s_setprio(1);
-      const __bf16* ktile = &lds_k[slot][0];
-      const __bf16* vtile = dead_prev ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
-      l_run += mfma_phase(ktile, vtile, koff, voff, qv, pb, s_hi, c, m_use, s, o);
-      __builtin_amdgcn_s_setprio(0);
-      phase_barrier();
-
-      // ---- VALU phase ------------------------------------------------------
-      if (!dead) {
-        if ((t_end - t0 < kN) || (p.causal && t_end - 1 > wave_qpos_min))
-          mask_tile(s, p.causal != 0, wave_qpos_min - t0, t0, t_end, lq, hh);
-        float mx0 = s[0][0], mx1 = s[1][0];
-#pragma unroll
-        for (int r = 1; r < 15; r += 2) {
-          mx0 = vmax(vmax(mx0, s[0][r]), s[0][r + 1]);
-          mx1 = vmax(vmax(mx1, s[1][r]), s[1][r + 1]);
+      if (t < 8) {
+        if (kk == 0) {
+          qk_mfma0(s[0][0], ka[t % 3], qv[0][kk]);
+          qk_mfma0(s[0][1], ka[t % 3], qv[1][kk]);
+        } else {
+          qk_mfma(s[0][0], ka[t % 3], qv[0][kk]);
+          qk_mfma(s[0][1], ka[t % 3], qv[1][kk]);
         }
-        const float mx = vmax(vmax(mx0, s[0][15]), vmax(mx1, s[1][15]));
-        m_tile = lane_swap32_max(mx) * c;
-        // Wave-uniform decision to move the reference max.
-        move_ref = __builtin_amdgcn_ballot_w64(m_tile > m_ref + kRescaleSlack) != 0;
-        if (move_ref) break;
+        exp_pair(s[1][0], 2 * kk, c, m_use[0], pb[0][2 + (kk >> 2)], (2 * kk) & 7, rh[0]);
+      } else if (t < 16) {
+        if (kk == 0) qk_mfma0(s[1][0], ka[t % 3], qv[0][kk]);
+        else qk_mfma(s[1][0], ka[t % 3], qv[0][kk]);
+        const int i = t - 8;
+        exp_pair(s[1][1], 2 * i, c, m_use[1], pb[1][2 + (i >> 2)], (2 * i) & 7, rh[1]);
+      } else {
+        if (kk == 0) qk_mfma0(s[1][1], ka[t % 3], qv[1][kk]);
+        else qk_mfma(s[1][1], ka[t % 3], qv[1][kk]);
+        mx[0] = vmax(vmax(mx[0], s[0][0][2 * kk]), s[0][0][2 * kk + 1]);
+        mx[1] = vmax(vmax(mx[1], s[0][1][2 * kk]), s[0][1][2 * kk + 1]);
       }
-      valu_rest();
-    } while (have);
-    if (!move_ref) break;
-    // Rare: move the reference max of this tile's rows and rescale O and l.
-    {
-      const float m_new = fmaxf(m_ref, m_tile);
-      const float alpha = exp2_fast(m_new == m_ref ? 0.f : m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      if ((t & 1) && t < 8) copy_one(kdst + 1024u * (t >> 1), ksrc, cl.k_off[t >> 1]);
+      if ((t & 1) && t >= 8 && t < 16)
+        copy_one(vdst + 1024u * ((t - 8) >> 1), vsrc + (size_t)(4 * ((t - 8) >> 1)) * p.v_ss,
+                 cl.v_off);
     }
-    valu_rest();
+    __builtin_amdgcn_sched_barrier(0);
+    // Tile j-1 is committed (unless stopping): its sums join the row sums.
+    l_run[0] += flag ? 0.f : rs_pend[0] + rh[0];
+    l_run[1] += flag ? 0.f : rs_pend[1] + rh[1];
+    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
+    // ---- Q3, Q4: O += P V of tile j-1 (step st: keys 16*(st/4).., d
+    // block st%4) ------------------------------------------------------
+    //  Q3: max of key block 1 (then the reference); exp of tile j, key
+    //      block 0, qb 1 (into pn: pb[1][0..1] is still being read).
+    //  Q4: exp of tile j, key block 0, qb 0.
+    bf16x8 va[3];
+    va[0] = read_v(vtile, voff, 0, 0);
+    va[1] = read_v(vtile, voff, 0, 1);
+    matrix_settle();  // the max reads s[1][1], written by the last op above
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int n = st + 2;
+      va[n % 3] = read_v(vtile, voff, n >> 2, n & 3);
+      pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
+      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mx[0] = vmax(mx[0], s[1][0][4 * st + r]);
+        mx[1] = vmax(mx[1], s[1][1][4 * st + r]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      bool far = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_tile = lane_swap32_max(mx[qb]) * c;
+        // No reference yet (the first tile): set it, nothing to rescale.
+        m_ref[qb] = m_ref[qb] == -INFINITY ? m_tile : m_ref[qb];
+        m_use[qb] = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
+        const bool far_q = m_tile > m_ref[qb] + kRescaleSlack;
+        // Such a tile is thrown away; this keeps its probabilities (and
+        // those of the tiles up to the stop) at most 1, so that the zero V
+        // tile turns them into exact zeros.
+        m_use[qb] = far_q ? fmaxf(m_use[qb], m_tile) : m_use[qb];
+        far = far || far_q;
+      }
+      if (__builtin_amdgcn_ballot_w64(far) != 0 && lane == 0)
+        __atomic_store_n(&lds_flag, 1, __ATOMIC_RELAXED);
+    }
+    bf16x8 pn[2];  // P of tile j, key block 0, qb 1
+    rs_pend[0] = 0.f;
+    rs_pend[1] = 0.f;
+#pragma unroll
+    for (int st = 4; st < 16; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < 16) {
+        const int n = st + 2;
+        va[n % 3] = read_v(vtile, voff, n >> 2, n & 3);
+      }
+      pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
+      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      if (st < 8) {
+        // qb 1, key block 0: pairs 0..7 over steps 4..7 (two per step).
+        const int i = 2 * (st - 4);
+        exp_pair(s[0][1], 2 * i, c, m_use[1], pn[i >> 2], (2 * i) & 7, rs_pend[1]);
+        exp_pair(s[0][1], 2 * i + 2, c, m_use[1], pn[(i + 1) >> 2], (2 * i + 2) & 7,
+                 rs_pend[1]);
+      } else {
+        // qb 0, key block 0 (pb[0][0..1] was last read at steps 4..7).
+        const int i = st - 8;
+        exp_pair(s[0][0], 2 * i, c, m_use[0], pb[0][i >> 2], (2 * i) & 7, rs_pend[0]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pb[1][0] = pn[0];
+    pb[1][1] = pn[1];
+    dead_prev = false;
+
+    // Copies still allowed in flight: those issued after K[j+1] and V[j],
+    // i.e. K[j+2], V[j+1], K[j+3], V[j+2].
+    wait_copies(16);
+    asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]),
+                 "+v"(rs_pend[0]), "+v"(rs_pend[1])
+                 :
+                 : "memory");
+    tile_barrier();
+    slot = (slot + 1) & (kRing - 1);
+    if (flag) {
+      stopped_at = it;
+      break;
+    }
   }
-  if (!group_b) phase_barrier();  // match group B's extra barrier
+  // Stopped early, or asked to stop at the last tile: the rest loop takes
+  // over from the tile that asked.
+  wait_copies(0);
+  const bool late = __atomic_load_n(&lds_flag, __ATOMIC_RELAXED) != 0;
+  const bool stop = stopped_at < n_tiles || late;
+  const int resume = stopped_at < n_tiles ? stopped_at - 1 : (late ? n_tiles - 1 : n_tiles);
 
-  // The last tile: second half of its softmax, then its P V (V[T-1] sits in
-  // the slot before `slot`).
-  l_run += softmax_hi(pb, s_hi, c, m_use);
-  pv_tile(dead_prev ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0], voff, pb, o);
+  // The last tile of the main walk (unless stopped): its key-block-1
+  // probabilities, then its P V (its V sits in the slot before `slot`).
+  {
+    // After a stop the pending tile is redone below: its P (finite) meets
+    // the zero V tile and its sums are dropped.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float rh = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        exp_pair(s[1][qb], 2 * i, c, m_use[qb], pb[qb][2 + (i >> 2)], (2 * i) & 7, rh);
+      l_run[qb] += stop ? 0.f : rs_pend[qb] + rh;
+    }
+    const __bf16* vtile =
+        (dead_prev || stop) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 va = read_v(vtile, voff, st >> 2, st & 3);
+      pv_mfma(o[0][st & 3], va, pb[0][st >> 2]);
+      pv_mfma(o[1][st & 3], va, pb[1][st >> 2]);
+    }
+  }
 
+  // ---- The rest, one tile at a time in slot 0, with masking and a per-row
+  // move of the reference: main-walk tiles from `resume` on (none unless
+  // stopped), then the causal diagonal band and ragged ends.
+  const int n_main_rest = n_tiles - resume;
+  for (int xt = 0; xt < n_main_rest + rest_walk.n; ++xt) {
+    const bool from_main = xt < n_main_rest;
+    Walk wk;
+    wk.a0 = from_main ? walk.a0 : rest_walk.a0;
+    wk.a_end = from_main ? walk.a_end : rest_walk.a_end;
+    wk.b0 = from_main ? walk.b0 : rest_walk.b0;
+    wk.b_end = from_main ? walk.b_end : rest_walk.b_end;
+    wk.n_a = from_main ? walk.n_a : rest_walk.n_a;
+    wk.n = from_main ? walk.n : rest_walk.n;
+    const int wi = xt < n_main_rest ? resume + xt : xt - n_main_rest;
+    int t0, t_end;
+    tile_bounds(wk, wi, t0, t_end);
+    tile_barrier();  // every wave is done with the previous tile's LDS
+    copy_tile_k(k_copy(wk, wi, 0));
+    copy_tile_v(v_copy(wk, wi, 0));
+    wait_copies(0);
+    tile_barrier();
+    const __bf16* ktile = &lds_k[0][0];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int kb = t >> 3, kk = t & 7;
+      const bf16x8 ka = read_k(ktile, koff, kb, kk);
+      if (kk == 0) {
+        qk_mfma0(s[kb][0], ka, qv[0][kk]);
+        qk_mfma0(s[kb][1], ka, qv[1][kk]);
+      } else {
+        qk_mfma(s[kb][0], ka, qv[0][kk]);
+        qk_mfma(s[kb][1], ka, qv[1][kk]);
+      }
+    }
+    matrix_settle();
+    const int last = t_end - 1 - t0;
+    const bool dead = (p.causal && t0 > wave_q_max) || wave_q0 >= p.seq_q;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      mask_block(s[0][qb], s[1][qb], p.causal != 0, rel_block(wave_q0 + 32 * qb) - t0, last, lq, hh);
+      float mxq = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mxq = vmax(vmax(mxq, s[0][qb][r]), s[1][qb][r]);
+      const float m_tile = lane_swap32_max(mxq) * c;
+      const bool move = m_tile > m_ref[qb];
+      const float m_new = move ? m_tile : m_ref[qb];
+      const float alpha = move ? exp2_fast(m_ref[qb] - m_new) : 1.f;
+      m_ref[qb] = m_new;
+      m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        __builtin_amdgcn_sched_barrier(0);
+        agpr_set(o[qb][db], agpr_get(o[qb][db]) * alpha);
+      }
+      float rsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        exp_pair(s[i >> 3][qb], 2 * (i & 7), c, m_use[qb], pb[qb][i >> 2], (2 * i) & 7, rsum);
+      l_run[qb] += rsum;
+    }
+    // P V; a wave none of whose queries sees the tile reads the zero tile.
+    const __bf16* vtile = dead ? lds_vzero : &lds_v[0][0];
+    matrix_settle();
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 va = read_v(vtile, voff, st >> 2, st & 3);
+      pv_mfma(o[0][st & 3], va, pb[0][st >> 2]);
+      pv_mfma(o[1][st & 3], va, pb[1][st >> 2]);
+    }
+    matrix_settle();
+  }
+
+  matrix_settle();
   // Finalise: O = acc / l, LSE = (m_ref + log2 l) ln 2; l == 0 means no
   // visible key (O = 0, LSE = -inf).  NaN in l propagates.
-  const float l_tot = lane_swap32_add(l_run);
-  const bool empty = l_tot == 0.f;
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  const float lse = empty ? -INFINITY : (m_ref + __log2f(l_tot)) * 0.69314718055994530942f;
-  const int64_t my_q = wave_q0 + lq;
-  if (my_q < p.seq_q) {
-    TOut* orow = (TOut*)p.o + b * p.o_sb + h * p.o_sh + my_q * p.o_ss;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = lane_swap32_add(l_run[qb]);
+    const bool empty = l_tot == 0.f;
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse = empty ? -INFINITY : (m_ref[qb] + __log2f(l_tot)) * 0.69314718055994530942f;
+    const int64_t my_q = wave_q0 + 32 * qb + lq;
+    if (my_q < p.seq_q) {
+      TOut* orow = (TOut*)p.o + b * p.o_sb + h * p.o_sh + my_q * p.o_ss;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        f32x4 v = {o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
-                   o[db][4 * gq + 3] * inv};
-        store4<TOut>(orow + db * 32 + 8 * gq + 4 * hh, v);
+      for (int db = 0; db < 4; ++db) {
+        const f32x16 ov = agpr_get(o[qb][db]);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          f32x4 v = {ov[4 * gq] * inv, ov[4 * gq + 1] * inv, ov[4 * gq + 2] * inv,
+                     ov[4 * gq + 3] * inv};
+          store4<TOut>(orow + db * 32 + 8 * gq + 4 * hh, v);
+        }
       }
-    if (hh == 0) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
+      if (hh == 0) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
+    }
   }
 }
 
