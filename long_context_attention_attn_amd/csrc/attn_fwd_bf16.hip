@@ -150,9 +150,11 @@ __device__ __forceinline__ void wait_copies(int n) {
 // Workgroup barrier without the release fence __syncthreads() adds: that
 // fence would wait for every global->LDS copy in flight, including the
 // prefetches of later tiles.  Copies a barrier must publish are waited for
-// explicitly with wait_copies(); LDS reads before a barrier have all returned
-// (their data fed matrix-core ops).
-__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// explicitly with wait_copies().  The wave's own LDS operations (reads, and
+// the stop flag's store) are complete before it arrives.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Global -> LDS copy of one 64-row tile of K or V by the four waves.  Wave w
 // copies rows 16*w .. 16*w+15 with four 1 KB instructions; lane i of
@@ -381,8 +383,12 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // the tile (P known to be zero), so that non-finite values in a V tile no
   // query of the wave can see never reach it through 0 * NaN.
   __shared__ __attribute__((aligned(16))) __bf16 lds_vzero[kTile];
-  // Set by a wave whose scores outgrow the reference: all waves start over.
-  __shared__ int lds_flag;
+  // Set by a wave whose scores outgrow the reference: all waves stop the
+  // main walk.  Tile j writes flag[j & 1], tile j+1 reads it after the
+  // barrier between them; a wave can write that flag again only in tile
+  // j+2, after the barrier that every wave reaches once it has read it, so
+  // all waves read the same value (and stop after the same tile).
+  __shared__ __attribute__((aligned(8))) int lds_flag[2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in [0, 4)
@@ -542,7 +548,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][qb][r] = -INFINITY;
   }
-  if (tid == 0) __atomic_store_n(&lds_flag, 0, __ATOMIC_RELAXED);
+  if (tid == 0) {
+    __atomic_store_n(&lds_flag[0], 0, __ATOMIC_RELAXED);
+    __atomic_store_n(&lds_flag[1], 0, __ATOMIC_RELAXED);
+  }
   // The compiler must not know P's starting value: a known constant gets
   // rebuilt by vector moves right in front of the asm matrix ops, which do
   // not see the wait states such a move needs before a matrix-core read.
@@ -585,8 +594,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     // Set by a wave at tile j-1 (before the last barrier): tile j-1's P V
     // then reads the zero tile, its sums are dropped, and the walk stops
     // after this tile; the rest loop redoes it from tile j-1.
-    const bool flag = __builtin_amdgcn_readfirstlane(
-                          __atomic_load_n(&lds_flag, __ATOMIC_RELAXED)) != 0;
+    // Both flags in one read at a fixed address; the previous tile's by parity.
+    const uint64_t both = __atomic_load_n((const uint64_t*)&lds_flag[0], __ATOMIC_RELAXED);
+    const int f_prev = (it & 1) ? (int)(uint32_t)both : (int)(uint32_t)(both >> 32);
+    const bool flag = __builtin_amdgcn_readfirstlane(f_prev) != 0;
     const __bf16* vtile =
         (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
     float rh[2] = {0.f, 0.f};  // sums of tile j-1, key block 1
@@ -678,7 +689,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         far = far || far_q;
       }
       if (__builtin_amdgcn_ballot_w64(far) != 0 && lane == 0)
-        __atomic_store_n(&lds_flag, 1, __ATOMIC_RELAXED);
+        __atomic_store_n(&lds_flag[it & 1], 1, __ATOMIC_RELAXED);
     }
     bf16x8 pn[2];  // P of tile j, key block 0, qb 1
     rs_pend[0] = 0.f;
@@ -726,7 +737,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // Stopped early, or asked to stop at the last tile: the rest loop takes
   // over from the tile that asked.
   wait_copies(0);
-  const bool late = __atomic_load_n(&lds_flag, __ATOMIC_RELAXED) != 0;
+  // The last tile's flag (flag[1] is never written when there is no tile).
+  const bool late = __atomic_load_n(&lds_flag[(n_tiles + 1) & 1], __ATOMIC_RELAXED) != 0;
   const bool stop = stopped_at < n_tiles || late;
   const int resume = stopped_at < n_tiles ? stopped_at - 1 : (late ? n_tiles - 1 : n_tiles);
 

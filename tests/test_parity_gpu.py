@@ -322,3 +322,44 @@ def test_strided_inputs():
                                       q_pos0=352)
     assert _max_err(o, o_ref) <= 2e-2
     _check_lse(lse, lse_ref)
+
+
+FAR_CASES = [
+    # (name, key rows made large (start, end, size), query rows that see them large)
+    ("mid_walk", [(768, 832, 32.0)], None),
+    ("last_main_tile", [(448, 512, 32.0)], None),
+    ("diagonal_band", [(1856, 1920, 32.0)], None),
+    ("two_jumps", [(768, 832, 32.0), (1088, 1152, 48.0)], None),
+    ("one_wave_only", [(1088, 1152, 32.0)], (128, 192)),
+]
+
+
+@pytest.mark.parametrize("din", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", FAR_CASES, ids=lambda c: c[0])
+def test_scores_far_above_the_first_tile(case, din):
+    """Keys whose scores lie ~130 (log2 units) above everything seen before
+    them in visit order: the running reference has to move by far more than
+    any working slack, mid-walk, at the walk's last full tile, inside the
+    causal diagonal band, twice, or for one 64-row group of queries only.
+    With C = 512 and rank 1 the visit order is rows 512..2047, then 0..511.
+    The second jump adds 45 (raw score units) on top of the first; it is kept
+    that small because an fp32 dot product of magnitude ~2000 already carries
+    rounding error near the fp32 path's 1e-4 output tolerance."""
+    name, jumps, qrows = case
+    _say(f"far scores {name} {din}")
+    b, hq, hkv, sq, skv, nch, rank, q_pos0 = 1, 4, 1, 256, 2048, 4, 1, 1792
+    q, k, v = gen_qkv(batch=b, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=din, device=DEV, seed=21)
+    k[..., 0] = 0
+    q[..., 0] = 0
+    r0, r1 = qrows if qrows else (0, sq)
+    q[:, :, r0:r1, 0] = 32.0
+    for a, e, size in jumps:
+        k[:, :, a:e, 0] = size
+    o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=nch, rank=rank, causal=True,
+                                      q_pos0=q_pos0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=True, q_pos0=q_pos0)
+    assert float(np.max(lse_ref)) > 60.0, "the case must actually reach large scores"
+    assert _max_err(o, o_ref) <= TOL_O[din], name
+    _check_lse(lse, lse_ref)
