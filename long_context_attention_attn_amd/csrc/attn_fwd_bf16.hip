@@ -168,6 +168,7 @@ __device__ __forceinline__ void tile_barrier() {
 struct CopyLanes {
   uint32_t k_off[4];  // K: byte offset of instruction n's source in a full tile
   uint32_t v_off;     // V: byte offset within 4 rows, same for every n
+  uint32_t v_offn[4]; // V: v_off plus 4 n rows (full tiles)
 };
 
 __device__ __forceinline__ uint32_t k_chunk(int row, int lane) {
@@ -186,6 +187,8 @@ __device__ __forceinline__ void copy_lanes_init(CopyLanes& cl, int w, int lane, 
   }
   const int row0 = 16 * w + (lane >> 4);
   cl.v_off = (uint32_t)row0 * v_stride_b + v_chunk(row0, lane);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) cl.v_offn[n] = cl.v_off + (uint32_t)(4 * n) * v_stride_b;
 }
 
 // One 1 KB copy instruction.  Written as inline assembly on purpose: through
@@ -203,6 +206,24 @@ __device__ __forceinline__ void copy_one(uint32_t lds_addr, const __bf16* gbase,
       :
       : "s"(lds_addr), "v"(off), "s"(gbase)
       : "memory", "m0");
+}
+
+// The same copy in two parts, for the hot loop: M0 is written one schedule
+// step before the load that reads it (no wait states to fill).
+__device__ __forceinline__ void set_m0(uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0" : : "s"(lds_addr) : "m0");
+}
+__device__ __forceinline__ void copy_at_m0(const __bf16* gbase, uint32_t off) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(gbase) : "memory");
+}
+
+// A wave-uniform pointer, kept in SGPRs (the copy instructions take their
+// base address from SGPRs).
+__device__ __forceinline__ const __bf16* uniform_ptr(const __bf16* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const __bf16*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
@@ -314,14 +335,22 @@ __device__ __forceinline__ void matrix_settle() {
 // bf16 into P operand slots x, x+1 of `dst`; their fp32 values are added to
 // `acc`.  (Summing the bf16 values instead would leave rows with few keys
 // with a relative error of up to 2^-9 in the sum, i.e. in the LSE.)
-__device__ __forceinline__ void exp_pair(const f32x16& s, int r, float c, float m, bf16x8& dst,
-                                         int x, float& acc) {
-  const float e0 = exp2_fast(fmaf(s[r], c, -m));
-  const float e1 = exp2_fast(fmaf(s[r + 1], c, -m));
+__device__ __forceinline__ float exp_one(const f32x16& s, int r, float c, float m) {
+  return exp2_fast(fmaf(s[r], c, -m));
+}
+// Stores two probabilities as bf16 into P^T (elements x, x+1) and adds them
+// to this lane's row sum (fp32, unrounded).
+__device__ __forceinline__ void store_pair(float e0, float e1, bf16x8& dst, int x, float& acc) {
   dst[x] = (__bf16)e0;
   dst[x + 1] = (__bf16)e1;
   acc += e0 + e1;
   asm volatile("" : "+v"(acc));
+}
+__device__ __forceinline__ void exp_pair(const f32x16& s, int r, float c, float m, bf16x8& dst,
+                                         int x, float& acc) {
+  const float e0 = exp_one(s, r, c, m);
+  const float e1 = exp_one(s, r + 1, c, m);
+  store_pair(e0, e1, dst, x, acc);
 }
 
 // NaN-propagating maximum (v_maximum3_f32 on gfx950; unlike fmaxf it needs
@@ -525,6 +554,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   }
   f32x16 o[2][4];
   float m_ref[2], m_use[2];  // reference max; m_use = m_ref, or 0 while it is -inf
+  float t_raw[2];            // (m_ref + slack) / c: a raw score above it is far
+  const float inv_c = 1.f / c;
   float l_run[2];            // this lane's half of the row sums
   // P^T operands: pb[qb][ks] holds keys 16*ks .. 16*ks+15 of the tile being
   // multiplied into O (ks 0-1: key block 0, ks 2-3: key block 1).
@@ -538,6 +569,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], (f32x16){});
     m_ref[qb] = -INFINITY;
     m_use[qb] = 0.f;
+    t_raw[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -579,15 +611,21 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   float rs_pend[2] = {0.f, 0.f};  // key-block-0 sums of tile j-1
   int it = 0;
   int stopped_at = n_tiles;  // iteration whose start saw a request to stop
+  // Sources of the next K and V tile copies (tiles it+3 and it+2, clamped to
+  // the last tile), advanced by one tile per iteration.
+  auto main_tile_src = [&](const __bf16* base, int64_t ss, int i) {
+    return base + (int64_t)(i < walk.n_a ? walk.a0 + kN * i : kN * (i - walk.n_a)) * ss;
+  };
+  int k_next_i = min(3, n_tiles - 1), v_next_i = min(2, n_tiles - 1);
+  const __bf16* k_next = main_tile_src(kbase, p.k_ss, max(k_next_i, 0));
+  const __bf16* v_next = main_tile_src(vbase, p.v_ss, max(v_next_i, 0));
+  const int64_t k_tile_step = (int64_t)kN * p.k_ss, v_tile_step = (int64_t)kN * p.v_ss;
   for (; it < n_tiles; ++it) {
     // This tile copies K tile j+3 and V tile j+2 (main-walk tiles are full:
     // no row clamping).  Past the end of the walk the last tile is copied
     // again, into a ring slot no later read uses.
-    const int kt = min(it + 3, n_tiles - 1), vt = min(it + 2, n_tiles - 1);
-    const __bf16* ksrc =
-        kbase + (int64_t)(kt < walk.n_a ? walk.a0 + kN * kt : kN * (kt - walk.n_a)) * p.k_ss;
-    const __bf16* vsrc =
-        vbase + (int64_t)(vt < walk.n_a ? walk.a0 + kN * vt : kN * (vt - walk.n_a)) * p.v_ss;
+    const __bf16* ksrc = k_next;
+    const __bf16* vsrc = v_next;
     const uint32_t kdst = k_ring + (uint32_t)((slot + 3) & (kRing - 1)) * kTileBytes;
     const uint32_t vdst = v_ring + (uint32_t)((slot + 2) & (kRing - 1)) * kTileBytes;
     const __bf16* ktile = &lds_k[slot][0];
@@ -621,14 +659,19 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         ka[u % 3] = read_k(ktile, koff, u >= 8 ? 1 : 0, u & 7);
       }
       if (t < 8) {
-        if (kk == 0) {
-          qk_mfma0(s[0][0], ka[t % 3], qv[0][kk]);
-          qk_mfma0(s[0][1], ka[t % 3], qv[1][kk]);
-        } else {
-          qk_mfma(s[0][0], ka[t % 3], qv[0][kk]);
-          qk_mfma(s[0][1], ka[t % 3], qv[1][kk]);
-        }
-        exp_pair(s[1][0], 2 * kk, c, m_use[0], pb[0][2 + (kk >> 2)], (2 * kk) & 7, rh[0]);
+        // Two half steps of one matrix op each, the vector work split
+        // between them, so that no op waits behind another in the issue
+        // order.
+        if (kk == 0) qk_mfma0(s[0][0], ka[t % 3], qv[0][kk]);
+        else qk_mfma(s[0][0], ka[t % 3], qv[0][kk]);
+        const float e0 = exp_one(s[1][0], 2 * kk, c, m_use[0]);
+        if (!(t & 1)) set_m0(kdst + 1024u * (t >> 1));
+        else copy_at_m0(ksrc, cl.k_off[t >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk == 0) qk_mfma0(s[0][1], ka[t % 3], qv[1][kk]);
+        else qk_mfma(s[0][1], ka[t % 3], qv[1][kk]);
+        const float e1 = exp_one(s[1][0], 2 * kk + 1, c, m_use[0]);
+        store_pair(e0, e1, pb[0][2 + (kk >> 2)], (2 * kk) & 7, rh[0]);
       } else if (t < 16) {
         if (kk == 0) qk_mfma0(s[1][0], ka[t % 3], qv[0][kk]);
         else qk_mfma(s[1][0], ka[t % 3], qv[0][kk]);
@@ -640,10 +683,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         mx[0] = vmax(vmax(mx[0], s[0][0][2 * kk]), s[0][0][2 * kk + 1]);
         mx[1] = vmax(vmax(mx[1], s[0][1][2 * kk]), s[0][1][2 * kk + 1]);
       }
-      if ((t & 1) && t < 8) copy_one(kdst + 1024u * (t >> 1), ksrc, cl.k_off[t >> 1]);
-      if ((t & 1) && t >= 8 && t < 16)
-        copy_one(vdst + 1024u * ((t - 8) >> 1), vsrc + (size_t)(4 * ((t - 8) >> 1)) * p.v_ss,
-                 cl.v_off);
+      if (!(t & 1) && t >= 8 && t < 16) set_m0(vdst + 1024u * ((t - 8) >> 1));
+      if ((t & 1) && t >= 8 && t < 16) copy_at_m0(vsrc, cl.v_offn[(t - 8) >> 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
     // Tile j-1 is committed (unless stopping): its sums join the row sums.
@@ -665,27 +706,32 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       const int n = st + 2;
       va[n % 3] = read_v(vtile, voff, n >> 2, n & 3);
       pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx[0] = vmax(mx[0], s[1][0][4 * st + r]);
+      __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mx[0] = vmax(mx[0], s[1][0][4 * st + r]);
-        mx[1] = vmax(mx[1], s[1][1][4 * st + r]);
-      }
+      for (int r = 0; r < 4; ++r) mx[1] = vmax(mx[1], s[1][1][4 * st + r]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    {
+    // Common case: no lane's partial max exceeds its row's threshold (the
+    // reference plus the slack, in raw score units; -inf before the first
+    // tile, so that tile always takes the branch).
+    if (__builtin_amdgcn_ballot_w64(mx[0] > t_raw[0] || mx[1] > t_raw[1]) != 0) {
       bool far = false;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float m_tile = lane_swap32_max(mx[qb]) * c;
         // No reference yet (the first tile): set it, nothing to rescale.
-        m_ref[qb] = m_ref[qb] == -INFINITY ? m_tile : m_ref[qb];
-        m_use[qb] = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
-        const bool far_q = m_tile > m_ref[qb] + kRescaleSlack;
-        // Such a tile is thrown away; this keeps its probabilities (and
+        const bool first = m_ref[qb] == -INFINITY;
+        const bool far_q = !first && m_tile > m_ref[qb] + kRescaleSlack;
+        m_ref[qb] = first ? m_tile : m_ref[qb];
+        // A far tile is thrown away; this keeps its probabilities (and
         // those of the tiles up to the stop) at most 1, so that the zero V
         // tile turns them into exact zeros.
-        m_use[qb] = far_q ? fmaxf(m_use[qb], m_tile) : m_use[qb];
+        m_use[qb] = first ? (m_tile == -INFINITY ? 0.f : m_tile)
+                          : (far_q ? fmaxf(m_use[qb], m_tile) : m_use[qb]);
+        t_raw[qb] = (m_ref[qb] + kRescaleSlack) * inv_c;
         far = far || far_q;
       }
       if (__builtin_amdgcn_ballot_w64(far) != 0 && lane == 0)
@@ -702,23 +748,38 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         va[n % 3] = read_v(vtile, voff, n >> 2, n & 3);
       }
       pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
-      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      float e0 = 0.f;
       if (st < 8) {
-        // qb 1, key block 0: pairs 0..7 over steps 4..7 (two per step).
+        // qb 1, key block 0: pairs 0..7 over steps 4..7 (one per half step).
         const int i = 2 * (st - 4);
         exp_pair(s[0][1], 2 * i, c, m_use[1], pn[i >> 2], (2 * i) & 7, rs_pend[1]);
+      } else {
+        e0 = exp_one(s[0][0], 2 * (st - 8), c, m_use[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      if (st < 8) {
+        const int i = 2 * (st - 4);
         exp_pair(s[0][1], 2 * i + 2, c, m_use[1], pn[(i + 1) >> 2], (2 * i + 2) & 7,
                  rs_pend[1]);
       } else {
         // qb 0, key block 0 (pb[0][0..1] was last read at steps 4..7).
         const int i = st - 8;
-        exp_pair(s[0][0], 2 * i, c, m_use[0], pb[0][i >> 2], (2 * i) & 7, rs_pend[0]);
+        const float e1 = exp_one(s[0][0], 2 * i + 1, c, m_use[0]);
+        store_pair(e0, e1, pb[0][i >> 2], (2 * i) & 7, rs_pend[0]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     pb[1][0] = pn[0];
     pb[1][1] = pn[1];
     dead_prev = false;
+    {
+      const bool kmore = k_next_i + 1 < n_tiles, vmore = v_next_i + 1 < n_tiles;
+      k_next_i += kmore ? 1 : 0;
+      v_next_i += vmore ? 1 : 0;
+      k_next = uniform_ptr(!kmore ? k_next : (k_next_i == walk.n_a ? kbase : k_next + k_tile_step));
+      v_next = uniform_ptr(!vmore ? v_next : (v_next_i == walk.n_a ? vbase : v_next + v_tile_step));
+    }
 
     // Copies still allowed in flight: those issued after K[j+1] and V[j],
     // i.e. K[j+2], V[j+1], K[j+3], V[j+2].
