@@ -107,6 +107,11 @@ static_assert(kBlockM == kWaves * 64, "64 query rows per wave");
 // contiguous ranges, each cut into 64-row tiles from its start.  Tile
 // boundaries need not fall on chunk boundaries: the keys are taken in
 // exactly the visit order either way.
+template <int N>
+struct SlotC {
+  static constexpr int value = N;
+};
+
 struct Walk {
   int a0, a_end, b0, b_end, n_a, n;
 };
@@ -276,6 +281,17 @@ __device__ __forceinline__ bf16x8 read_k(const __bf16* ktile, const int (&koff)[
 // V^T operand of 16-key step ks, d block db: two transposing reads 8 rows
 // apart.  voff[db] is this lane's byte address for step 0; step ks is 16
 // rows (4 KB) further.
+// The same read from a per-lane LDS byte address computed once per tile
+// (the tile base plus voff[db]); the step goes into the instruction offset.
+__device__ __forceinline__ bf16x8 read_v_at(uint32_t addr, int ks) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(addr + ks * 4096));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(addr + ks * 4096 + 2048));
+  bf16x8 a;
+  a.lo = __builtin_bit_cast(bf16x4, lo);
+  a.hi = __builtin_bit_cast(bf16x4, hi);
+  return a;
+}
+
 __device__ __forceinline__ bf16x8 read_v(const __bf16* vtile, const int (&voff)[4], int ks,
                                          int db) {
   const char* src = (const char*)vtile + voff[db] + ks * 4096;
@@ -341,8 +357,12 @@ __device__ __forceinline__ float exp_one(const f32x16& s, int r, float c, float 
 // Stores two probabilities as bf16 into P^T (elements x, x+1) and adds them
 // to this lane's row sum (fp32, unrounded).
 __device__ __forceinline__ void store_pair(float e0, float e1, bf16x8& dst, int x, float& acc) {
-  dst[x] = (__bf16)e0;
-  dst[x + 1] = (__bf16)e1;
+  const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+  uint32_t u = __builtin_bit_cast(uint32_t, pr);
+  asm volatile("" : "+v"(u));  // round here, not where the matrix op reads it
+  u32x4 d = __builtin_bit_cast(u32x4, dst);
+  d[x >> 1] = u;
+  dst = __builtin_bit_cast(bf16x8, d);
   acc += e0 + e1;
   asm volatile("" : "+v"(acc));
 }
@@ -620,7 +640,12 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const __bf16* k_next = main_tile_src(kbase, p.k_ss, max(k_next_i, 0));
   const __bf16* v_next = main_tile_src(vbase, p.v_ss, max(v_next_i, 0));
   const int64_t k_tile_step = (int64_t)kN * p.k_ss, v_tile_step = (int64_t)kN * p.v_ss;
-  for (; it < n_tiles; ++it) {
+  // The hot loop's body for a tile whose ring slot (its index mod 4, and so
+  // the parity of its stop flag) is a compile-time constant: every LDS
+  // address below is then a register plus an immediate.  Returns true when
+  // the walk stops after this tile.
+  auto tile_body = [&](auto slot_c) -> bool {
+    constexpr int slot = decltype(slot_c)::value;
     // This tile copies K tile j+3 and V tile j+2 (main-walk tiles are full:
     // no row clamping).  Past the end of the walk the last tile is copied
     // again, into a ring slot no later read uses.
@@ -632,61 +657,86 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     // Set by a wave at tile j-1 (before the last barrier): tile j-1's P V
     // then reads the zero tile, its sums are dropped, and the walk stops
     // after this tile; the rest loop redoes it from tile j-1.
-    // Both flags in one read at a fixed address; the previous tile's by parity.
-    const uint64_t both = __atomic_load_n((const uint64_t*)&lds_flag[0], __ATOMIC_RELAXED);
-    const int f_prev = (it & 1) ? (int)(uint32_t)both : (int)(uint32_t)(both >> 32);
-    const bool flag = __builtin_amdgcn_readfirstlane(f_prev) != 0;
-    const __bf16* vtile =
-        (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
     float rh[2] = {0.f, 0.f};  // sums of tile j-1, key block 1
     float mx[2] = {-INFINITY, -INFINITY};
 
-    // ---- Q1, Q2: S of tile j.  Step t < 8: key block 0, d step t, both
-    // query blocks; 8 <= t < 16: key block 1 for qb 0; t >= 16: key block 1
-    // for qb 1 (its K operands read again, so that the old scores of qb 1
-    // are consumed before they are overwritten).  Alongside: exp of tile
-    // j-1, key block 1 (qb 0 in t < 8, qb 1 in 8 <= t < 16), copies of K
-    // tile j+3 and V tile j+2, and the max of key block 0 (t >= 16).
-    bf16x8 ka[3];
-    ka[0] = read_k(ktile, koff, 0, 0);
-    ka[1] = read_k(ktile, koff, 0, 1);
-#pragma unroll
-    for (int t = 0; t < 24; ++t) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int kk = t & 7;
-      if (t + 2 < 24) {
-        const int u = t + 2;
-        ka[u % 3] = read_k(ktile, koff, u >= 8 ? 1 : 0, u & 7);
-      }
-      if (t < 8) {
-        // Two half steps of one matrix op each, the vector work split
-        // between them, so that no op waits behind another in the issue
-        // order.
-        if (kk == 0) qk_mfma0(s[0][0], ka[t % 3], qv[0][kk]);
-        else qk_mfma(s[0][0], ka[t % 3], qv[0][kk]);
-        const float e0 = exp_one(s[1][0], 2 * kk, c, m_use[0]);
-        if (!(t & 1)) set_m0(kdst + 1024u * (t >> 1));
-        else copy_at_m0(ksrc, cl.k_off[t >> 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk == 0) qk_mfma0(s[0][1], ka[t % 3], qv[1][kk]);
-        else qk_mfma(s[0][1], ka[t % 3], qv[1][kk]);
-        const float e1 = exp_one(s[1][0], 2 * kk + 1, c, m_use[0]);
-        store_pair(e0, e1, pb[0][2 + (kk >> 2)], (2 * kk) & 7, rh[0]);
-      } else if (t < 16) {
-        if (kk == 0) qk_mfma0(s[1][0], ka[t % 3], qv[0][kk]);
-        else qk_mfma(s[1][0], ka[t % 3], qv[0][kk]);
-        const int i = t - 8;
-        exp_pair(s[1][1], 2 * i, c, m_use[1], pb[1][2 + (i >> 2)], (2 * i) & 7, rh[1]);
+    // ---- Q1, Q2: S of tile j in 32 half steps of one matrix op each, the
+    // two query blocks alternating on one K read.  Q1 (t < 8): key block 0,
+    // with the exponentials of tile j-1's key block 1 (both query blocks, one
+    // pair per half step; Q2 overwrites those scores).  Q2 (t >= 8): key
+    // block 1, with the key-block-0 maxima and the copies of K tile j+3 and
+    // V tile j+2 (one copy instruction per half step).
+    bf16x8 ka[4];
+    ka[0] = read_k(ktile, koff, 0 >> 3, 0 & 7);
+    ka[1] = read_k(ktile, koff, 1 >> 3, 1 & 7);
+    ka[2] = read_k(ktile, koff, 2 >> 3, 2 & 7);
+    // Both flags in one read at a fixed address (behind the first K reads;
+    // first used after Q2, so its latency is hidden).  Only this tile's
+    // writes could race with the read, and they go to the other word.
+    const uint64_t both = __atomic_load_n((const uint64_t*)&lds_flag[0], __ATOMIC_RELAXED);
+    float pe0 = 0.f, pe1 = 0.f;  // exponentials issued, not yet rounded and summed
+    auto copy_step = [&](int h) {  // h = 0..15: K copies 0..3, then V copies 0..3
+      if (h < 8) {
+        if (!(h & 1)) set_m0(kdst + 1024u * (h >> 1));
+        else copy_at_m0(ksrc, cl.k_off[h >> 1]);
       } else {
-        if (kk == 0) qk_mfma0(s[1][1], ka[t % 3], qv[1][kk]);
-        else qk_mfma(s[1][1], ka[t % 3], qv[1][kk]);
-        mx[0] = vmax(vmax(mx[0], s[0][0][2 * kk]), s[0][0][2 * kk + 1]);
-        mx[1] = vmax(vmax(mx[1], s[0][1][2 * kk]), s[0][1][2 * kk + 1]);
+        if (!(h & 1)) set_m0(vdst + 1024u * ((h - 8) >> 1));
+        else copy_at_m0(vsrc, cl.v_offn[(h - 8) >> 1]);
       }
-      if (!(t & 1) && t >= 8 && t < 16) set_m0(vdst + 1024u * ((t - 8) >> 1));
-      if ((t & 1) && t >= 8 && t < 16) copy_at_m0(vsrc, cl.v_offn[(t - 8) >> 1]);
+    };
+    // Key-block-0 max of query block qb, score pair p (2 scores per lane).
+    auto max_pair = [&](int qb, int p) {
+      mx[qb] = vmax(vmax(mx[qb], s[0][qb][2 * p]), s[0][qb][2 * p + 1]);
+    };
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int kb = t >> 3, kk = t & 7;
+      // Half step A: query block 0.
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 3 < 16) {
+        const int u = t + 3;
+        ka[u % 4] = read_k(ktile, koff, u >> 3, u & 7);
+      }
+      if (kk == 0) qk_mfma0(s[kb][0], ka[t % 4], qv[0][kk]);
+      else qk_mfma(s[kb][0], ka[t % 4], qv[0][kk]);
+      if (t < 8) {
+        // Exponentials of pair kk (qb 0) now, rounding and sums of the pair
+        // before it (qb 1, kk - 1) after them: an exponential's result is
+        // first used a half step later.
+        const float n0 = exp_one(s[1][0], 2 * kk, c, m_use[0]);
+        const float n1 = exp_one(s[1][0], 2 * kk + 1, c, m_use[0]);
+        if (t > 0) store_pair(pe0, pe1, pb[1][2 + ((kk - 1) >> 2)], (2 * (kk - 1)) & 7, rh[1]);
+        pe0 = n0;
+        pe1 = n1;
+      } else {
+        if (t == 8) store_pair(pe0, pe1, pb[1][3], 6, rh[1]);
+        copy_step(2 * (t - 8));
+        // qb 0's key-block-0 scores were last written in half step 7A; the
+        // first read waits for two full steps.
+        if (t >= 10) max_pair(0, t - 10);
+        if (t >= 14) max_pair(0, t - 8);
+      }
+      // Half step B: query block 1.
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) qk_mfma0(s[kb][1], ka[t % 4], qv[1][kk]);
+      else qk_mfma(s[kb][1], ka[t % 4], qv[1][kk]);
+      if (t < 8) {
+        const float n0 = exp_one(s[1][1], 2 * kk, c, m_use[1]);
+        const float n1 = exp_one(s[1][1], 2 * kk + 1, c, m_use[1]);
+        store_pair(pe0, pe1, pb[0][2 + (kk >> 2)], (2 * kk) & 7, rh[0]);
+        pe0 = n0;
+        pe1 = n1;
+      } else {
+        copy_step(2 * (t - 8) + 1);
+        if (t >= 11) max_pair(1, t - 11);
+        if (t >= 13) max_pair(1, t - 8);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
+    const int f_prev = (slot & 1) ? (int)(uint32_t)both : (int)(uint32_t)(both >> 32);
+    const bool flag = __builtin_amdgcn_readfirstlane(f_prev) != 0;
+    const __bf16* vtile =
+        (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
     // Tile j-1 is committed (unless stopping): its sums join the row sums.
     l_run[0] += flag ? 0.f : rs_pend[0] + rh[0];
     l_run[1] += flag ? 0.f : rs_pend[1] + rh[1];
@@ -696,22 +746,44 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     //  Q3: max of key block 1 (then the reference); exp of tile j, key
     //      block 0, qb 1 (into pn: pb[1][0..1] is still being read).
     //  Q4: exp of tile j, key block 0, qb 0.
-    bf16x8 va[3];
-    va[0] = read_v(vtile, voff, 0, 0);
-    va[1] = read_v(vtile, voff, 0, 1);
-    matrix_settle();  // the max reads s[1][1], written by the last op above
+    // This lane's V^T read addresses for the four d blocks of this tile.
+    uint32_t vaddr[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      vaddr[db] = lds_address(vtile) + (uint32_t)voff[db];
+      asm volatile("" : "+v"(vaddr[db]));
+    }
+    bf16x8 va[4];
+    va[0] = read_v_at(vaddr[0 & 3], 0 >> 2);
+    va[1] = read_v_at(vaddr[1 & 3], 1 >> 2);
+    va[2] = read_v_at(vaddr[2 & 3], 2 >> 2);
+    // Key-block-1 maxima: qb 0 first (its scores were final 8 ops before the
+    // end of Q2), qb 1 from the fifth half step on (its last op then lies
+    // four matrix ops and their vector work back).
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      const int n = st + 2;
-      va[n % 3] = read_v(vtile, voff, n >> 2, n & 3);
-      pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
+      const int n = st + 3;
+      va[n % 4] = read_v_at(vaddr[n & 3], n >> 2);
+      pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx[0] = vmax(mx[0], s[1][0][4 * st + r]);
+      for (int r = 0; r < 4; ++r) {
+        const int h = 2 * st;
+        if (h >= 4) {
+          mx[0] = vmax(mx[0], s[1][0][4 * (h - 4) + r]);
+          mx[1] = vmax(mx[1], s[1][1][4 * (h - 4) + r]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx[1] = vmax(mx[1], s[1][1][4 * st + r]);
+      for (int r = 0; r < 4; ++r) {
+        const int h = 2 * st + 1;
+        if (h >= 4) {
+          mx[0] = vmax(mx[0], s[1][0][4 * (h - 4) + r]);
+          mx[1] = vmax(mx[1], s[1][1][4 * (h - 4) + r]);
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // Common case: no lane's partial max exceeds its row's threshold (the
@@ -735,7 +807,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         far = far || far_q;
       }
       if (__builtin_amdgcn_ballot_w64(far) != 0 && lane == 0)
-        __atomic_store_n(&lds_flag[it & 1], 1, __ATOMIC_RELAXED);
+        __atomic_store_n(&lds_flag[slot & 1], 1, __ATOMIC_RELAXED);
     }
     bf16x8 pn[2];  // P of tile j, key block 0, qb 1
     rs_pend[0] = 0.f;
@@ -743,33 +815,45 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int st = 4; st < 16; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < 16) {
-        const int n = st + 2;
-        va[n % 3] = read_v(vtile, voff, n >> 2, n & 3);
+      if (st + 3 < 16) {
+        const int n = st + 3;
+        va[n % 4] = read_v_at(vaddr[n & 3], n >> 2);
       }
-      pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
-      float e0 = 0.f;
+      pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
+      // Exponentials are issued one half step before their rounding and
+      // sums.  qb 1, key block 0: pairs 0..7 in half steps 4A..7B; qb 0: pair
+      // st - 8 issued in half step B of steps 8..15 (pb[0][0..1] was last
+      // read in step 7), finished in the next half step A.
       if (st < 8) {
-        // qb 1, key block 0: pairs 0..7 over steps 4..7 (one per half step).
         const int i = 2 * (st - 4);
-        exp_pair(s[0][1], 2 * i, c, m_use[1], pn[i >> 2], (2 * i) & 7, rs_pend[1]);
+        const float n0 = exp_one(s[0][1], 2 * i, c, m_use[1]);
+        const float n1 = exp_one(s[0][1], 2 * i + 1, c, m_use[1]);
+        if (st > 4) store_pair(pe0, pe1, pn[(i - 1) >> 2], (2 * (i - 1)) & 7, rs_pend[1]);
+        pe0 = n0;
+        pe1 = n1;
+      } else if (st == 8) {
+        store_pair(pe0, pe1, pn[1], 6, rs_pend[1]);
       } else {
-        e0 = exp_one(s[0][0], 2 * (st - 8), c, m_use[0]);
+        const int i = st - 9;
+        store_pair(pe0, pe1, pb[0][i >> 2], (2 * i) & 7, rs_pend[0]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
       if (st < 8) {
-        const int i = 2 * (st - 4);
-        exp_pair(s[0][1], 2 * i + 2, c, m_use[1], pn[(i + 1) >> 2], (2 * i + 2) & 7,
-                 rs_pend[1]);
+        const int i = 2 * (st - 4) + 1;
+        const float n0 = exp_one(s[0][1], 2 * i, c, m_use[1]);
+        const float n1 = exp_one(s[0][1], 2 * i + 1, c, m_use[1]);
+        store_pair(pe0, pe1, pn[(i - 1) >> 2], (2 * (i - 1)) & 7, rs_pend[1]);
+        pe0 = n0;
+        pe1 = n1;
       } else {
-        // qb 0, key block 0 (pb[0][0..1] was last read at steps 4..7).
         const int i = st - 8;
-        const float e1 = exp_one(s[0][0], 2 * i + 1, c, m_use[0]);
-        store_pair(e0, e1, pb[0][i >> 2], (2 * i) & 7, rs_pend[0]);
+        pe0 = exp_one(s[0][0], 2 * i, c, m_use[0]);
+        pe1 = exp_one(s[0][0], 2 * i + 1, c, m_use[0]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    store_pair(pe0, pe1, pb[0][1], 6, rs_pend[0]);  // qb 0, pair 7
     pb[1][0] = pn[0];
     pb[1][1] = pn[1];
     dead_prev = false;
@@ -789,12 +873,24 @@ void attn_fwd_bf16_kernel(FwdParams p) {
                  :
                  : "memory");
     tile_barrier();
-    slot = (slot + 1) & (kRing - 1);
     if (flag) {
       stopped_at = it;
-      break;
+      return true;
     }
+    return false;
+  };
+  while (it < n_tiles) {
+    if (tile_body(SlotC<0>())) break;
+    if (++it >= n_tiles) break;
+    if (tile_body(SlotC<1>())) break;
+    if (++it >= n_tiles) break;
+    if (tile_body(SlotC<2>())) break;
+    if (++it >= n_tiles) break;
+    if (tile_body(SlotC<3>())) break;
+    ++it;
   }
+  // The slot after the last tile run (a stop at tile `it` ran it too).
+  slot = (stopped_at < n_tiles ? stopped_at + 1 : n_tiles) & (kRing - 1);
   // Stopped early, or asked to stop at the last tile: the rest loop takes
   // over from the tile that asked.
   wait_copies(0);
