@@ -28,20 +28,25 @@
 // register r): column = l % 32, row = 8*(r/4) + 4*(l/32) + (r%4).
 //
 // One wave per SIMD, so the overlap of matrix-core work and softmax work
-// comes from one instruction stream.  Tile j is processed in four quarters
-// of 16 matrix-core ops; each quarter also carries about a quarter of the
-// softmax work (exponentials of 16 scores per lane, partial row maxima):
-//   Q1: S[key block 0] of tile j      + exp of tile j-1, key block 1, qb 0
-//   Q2: S[key block 1] of tile j      + exp of tile j-1, key block 1, qb 1;
-//                                       max of tile j, key block 0
-//   Q3: O += P V, tile j-1, keys 0-31 + max of tile j, key block 1;
-//                                       exp of tile j, key block 0, qb 1
+// comes from one instruction stream, which issues at most one instruction
+// every few cycles.  Tile j is processed in 64 half steps of one matrix-core
+// op each (two ops back to back would leave the vector work behind the
+// second one waiting for the matrix pipe), the two query blocks alternating;
+// the softmax work rides along:
+//   Q1: S of tile j, key block 0   + exp of tile j-1, key block 1 (both qb)
+//   Q2: S of tile j, key block 1   + max of tile j, key block 0; all copies
+//   Q3: O += P V, tile j-1, keys 0-31  + max of key block 1, reference check;
+//                                        exp of tile j, key block 0, qb 1
 //   Q4: O += P V, tile j-1, keys 32-63 + exp of tile j, key block 0, qb 0
-// The order is fixed with scheduling barriers at every step.
-//
+// An exponential is rounded to bf16 and summed one half step after it is
+// issued, so that no vector op waits on a transcendental result; K and V
+// operands are read three steps ahead.  Scheduling barriers fix the order,
+// and the loop is unrolled by the ring depth so that ring slots are
+// compile-time constants.
+
 // K and V tiles stream straight from global memory into a 4-deep LDS ring
 // per tensor (global_load_lds_dwordx4, no registers involved): each wave
-// copies 16 rows of K tile j+3 and of V tile j+2 in Q1/Q2 (past the end of
+// copies 16 rows of K tile j+3 and of V tile j+2 in Q2 (past the end of
 // the walk, the last tile again into a slot nothing reads, so every tile
 // issues the same copies), waits for its own copies of the tiles the next
 // tile needs, then all waves meet at one barrier per tile.  A slot is
