@@ -371,6 +371,9 @@ __device__ __forceinline__ void store_pair(float e0, float e1, bf16x8& dst, int 
   acc += e0 + e1;
   asm volatile("" : "+v"(acc));
 }
+// Exponentials of scores already scaled and shifted in place (s*c - m).
+__device__ __forceinline__ float exp_s(const f32x16& s, int r) { return exp2_fast(s[r]); }
+
 __device__ __forceinline__ void exp_pair(const f32x16& s, int r, float c, float m, bf16x8& dst,
                                          int x, float& acc) {
   const float e0 = exp_one(s, r, c, m);
@@ -579,8 +582,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   }
   f32x16 o[2][4];
   float m_ref[2], m_use[2];  // reference max; m_use = m_ref, or 0 while it is -inf
-  float t_raw[2];            // (m_ref + slack) / c: a raw score above it is far
-  const float inv_c = 1.f / c;
+  // In the hot loop the scores are scaled and shifted in place, s*c - m_use,
+  // before their maxima are taken: a shifted score above t_far = m_ref +
+  // slack - m_use is far (-inf before the first tile, which so always
+  // takes the rare branch).
+  float t_far[2];
   float l_run[2];            // this lane's half of the row sums
   // P^T operands: pb[qb][ks] holds keys 16*ks .. 16*ks+15 of the tile being
   // multiplied into O (ks 0-1: key block 0, ks 2-3: key block 1).
@@ -594,7 +600,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], (f32x16){});
     m_ref[qb] = -INFINITY;
     m_use[qb] = 0.f;
-    t_raw[qb] = -INFINITY;
+    t_far[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -691,6 +697,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     };
     // Key-block-0 max of query block qb, score pair p (2 scores per lane).
     auto max_pair = [&](int qb, int p) {
+      s[0][qb][2 * p] = fmaf(s[0][qb][2 * p], c, -m_use[qb]);
+      s[0][qb][2 * p + 1] = fmaf(s[0][qb][2 * p + 1], c, -m_use[qb]);
       mx[qb] = vmax(vmax(mx[qb], s[0][qb][2 * p]), s[0][qb][2 * p + 1]);
     };
 #pragma unroll
@@ -708,8 +716,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         // Exponentials of pair kk (qb 0) now, rounding and sums of the pair
         // before it (qb 1, kk - 1) after them: an exponential's result is
         // first used a half step later.
-        const float n0 = exp_one(s[1][0], 2 * kk, c, m_use[0]);
-        const float n1 = exp_one(s[1][0], 2 * kk + 1, c, m_use[0]);
+        const float n0 = exp_s(s[1][0], 2 * kk);
+        const float n1 = exp_s(s[1][0], 2 * kk + 1);
         if (t > 0) store_pair(pe0, pe1, pb[1][2 + ((kk - 1) >> 2)], (2 * (kk - 1)) & 7, rh[1]);
         pe0 = n0;
         pe1 = n1;
@@ -726,8 +734,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       if (kk == 0) qk_mfma0(s[kb][1], ka[t % 4], qv[1][kk]);
       else qk_mfma(s[kb][1], ka[t % 4], qv[1][kk]);
       if (t < 8) {
-        const float n0 = exp_one(s[1][1], 2 * kk, c, m_use[1]);
-        const float n1 = exp_one(s[1][1], 2 * kk + 1, c, m_use[1]);
+        const float n0 = exp_s(s[1][1], 2 * kk);
+        const float n1 = exp_s(s[1][1], 2 * kk + 1);
         store_pair(pe0, pe1, pb[0][2 + (kk >> 2)], (2 * kk) & 7, rh[0]);
         pe0 = n0;
         pe1 = n1;
@@ -765,40 +773,38 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     // Key-block-1 maxima: qb 0 first (its scores were final 8 ops before the
     // end of Q2), qb 1 from the fifth half step on (its last op then lies
     // four matrix ops and their vector work back).
+    // Key block 1, half steps 4..11: scale and shift two scores per query
+    // block, then take their max.
+    auto scale_max_kb1 = [&](int h) {
+      if (h >= 4 && h < 12) {
+        const int r = 2 * (h - 4);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+        for (int qb = 0; qb < 2; ++qb) {
+          s[1][qb][r] = fmaf(s[1][qb][r], c, -m_use[qb]);
+          s[1][qb][r + 1] = fmaf(s[1][qb][r + 1], c, -m_use[qb]);
+          mx[qb] = vmax(vmax(mx[qb], s[1][qb][r]), s[1][qb][r + 1]);
+        }
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
       __builtin_amdgcn_sched_barrier(0);
       const int n = st + 3;
       va[n % 4] = read_v_at(vaddr[n & 3], n >> 2);
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 2 * st;
-        if (h >= 4) {
-          mx[0] = vmax(mx[0], s[1][0][4 * (h - 4) + r]);
-          mx[1] = vmax(mx[1], s[1][1][4 * (h - 4) + r]);
-        }
-      }
+      scale_max_kb1(2 * st);
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 2 * st + 1;
-        if (h >= 4) {
-          mx[0] = vmax(mx[0], s[1][0][4 * (h - 4) + r]);
-          mx[1] = vmax(mx[1], s[1][1][4 * (h - 4) + r]);
-        }
-      }
+      scale_max_kb1(2 * st + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Common case: no lane's partial max exceeds its row's threshold (the
-    // reference plus the slack, in raw score units; -inf before the first
-    // tile, so that tile always takes the branch).
-    if (__builtin_amdgcn_ballot_w64(mx[0] > t_raw[0] || mx[1] > t_raw[1]) != 0) {
+    // Common case: no lane's partial max exceeds its row's threshold.
+    if (__builtin_amdgcn_ballot_w64(mx[0] > t_far[0] || mx[1] > t_far[1]) != 0) {
       bool far = false;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float m_tile = lane_swap32_max(mx[qb]) * c;
+        const float m_old = m_use[qb];
+        const float m_tile = lane_swap32_max(mx[qb]) + m_old;  // max of s*c
         // No reference yet (the first tile): set it, nothing to rescale.
         const bool first = m_ref[qb] == -INFINITY;
         const bool far_q = !first && m_tile > m_ref[qb] + kRescaleSlack;
@@ -808,7 +814,15 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         // tile turns them into exact zeros.
         m_use[qb] = first ? (m_tile == -INFINITY ? 0.f : m_tile)
                           : (far_q ? fmaxf(m_use[qb], m_tile) : m_use[qb]);
-        t_raw[qb] = (m_ref[qb] + kRescaleSlack) * inv_c;
+        t_far[qb] = m_ref[qb] + kRescaleSlack - m_use[qb];
+        // The tile's scores were shifted by the old m_use: shift them to the
+        // new one.
+        const float d = m_old - m_use[qb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[0][qb][r] += d;
+          s[1][qb][r] += d;
+        }
         far = far || far_q;
       }
       if (__builtin_amdgcn_ballot_w64(far) != 0 && lane == 0)
@@ -817,48 +831,39 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     bf16x8 pn[2];  // P of tile j, key block 0, qb 1
     rs_pend[0] = 0.f;
     rs_pend[1] = 0.f;
+    // Exponentials of tile j, key block 0, one pair per half step from half
+    // step 12 (qb 1: pairs 0..7 into pn; qb 0 from half step 20: pb[0][0..1]
+    // was last read in step 7), each rounded and summed a half step later.
+    auto exp_job = [&](int h) {
+      const int j = h - 12;  // job index 0..15
+      float n0 = 0.f, n1 = 0.f;
+      if (j >= 0 && j < 16) {
+        const int qb = j < 8 ? 1 : 0, i = j & 7;
+        n0 = exp_s(s[0][qb], 2 * i);
+        n1 = exp_s(s[0][qb], 2 * i + 1);
+      }
+      if (j >= 1 && j <= 16) {
+        const int i = j - 1;  // commit job i
+        if (i < 8) store_pair(pe0, pe1, pn[i >> 2], (2 * i) & 7, rs_pend[1]);
+        else store_pair(pe0, pe1, pb[0][(i - 8) >> 2], (2 * (i - 8)) & 7, rs_pend[0]);
+      }
+      pe0 = n0;
+      pe1 = n1;
+    };
 #pragma unroll
-    for (int st = 4; st < 16; ++st) {
+    for (int st = 6; st < 16; ++st) {
       __builtin_amdgcn_sched_barrier(0);
       if (st + 3 < 16) {
         const int n = st + 3;
         va[n % 4] = read_v_at(vaddr[n & 3], n >> 2);
       }
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
-      // Exponentials are issued one half step before their rounding and
-      // sums.  qb 1, key block 0: pairs 0..7 in half steps 4A..7B; qb 0: pair
-      // st - 8 issued in half step B of steps 8..15 (pb[0][0..1] was last
-      // read in step 7), finished in the next half step A.
-      if (st < 8) {
-        const int i = 2 * (st - 4);
-        const float n0 = exp_one(s[0][1], 2 * i, c, m_use[1]);
-        const float n1 = exp_one(s[0][1], 2 * i + 1, c, m_use[1]);
-        if (st > 4) store_pair(pe0, pe1, pn[(i - 1) >> 2], (2 * (i - 1)) & 7, rs_pend[1]);
-        pe0 = n0;
-        pe1 = n1;
-      } else if (st == 8) {
-        store_pair(pe0, pe1, pn[1], 6, rs_pend[1]);
-      } else {
-        const int i = st - 9;
-        store_pair(pe0, pe1, pb[0][i >> 2], (2 * i) & 7, rs_pend[0]);
-      }
+      exp_job(2 * st);
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
-      if (st < 8) {
-        const int i = 2 * (st - 4) + 1;
-        const float n0 = exp_one(s[0][1], 2 * i, c, m_use[1]);
-        const float n1 = exp_one(s[0][1], 2 * i + 1, c, m_use[1]);
-        store_pair(pe0, pe1, pn[(i - 1) >> 2], (2 * (i - 1)) & 7, rs_pend[1]);
-        pe0 = n0;
-        pe1 = n1;
-      } else {
-        const int i = st - 8;
-        pe0 = exp_one(s[0][0], 2 * i, c, m_use[0]);
-        pe1 = exp_one(s[0][0], 2 * i + 1, c, m_use[0]);
-      }
+      exp_job(2 * st + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_pair(pe0, pe1, pb[0][1], 6, rs_pend[0]);  // qb 0, pair 7
     pb[1][0] = pn[0];
     pb[1][1] = pn[1];
     dead_prev = false;
@@ -914,7 +919,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       float rh = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        exp_pair(s[1][qb], 2 * i, c, m_use[qb], pb[qb][2 + (i >> 2)], (2 * i) & 7, rh);
+        store_pair(exp_s(s[1][qb], 2 * i), exp_s(s[1][qb], 2 * i + 1), pb[qb][2 + (i >> 2)],
+                   (2 * i) & 7, rh);
       l_run[qb] += stop ? 0.f : rs_pend[qb] + rh;
     }
     const __bf16* vtile =
