@@ -363,3 +363,65 @@ def test_scores_far_above_the_first_tile(case, din):
     assert float(np.max(lse_ref)) > 60.0, "the case must actually reach large scores"
     assert _max_err(o, o_ref) <= TOL_O[din], name
     _check_lse(lse, lse_ref)
+
+
+def _sweep_cases(n, seed):
+    """Small shifted-attention problems with every size drawn at random: GQA
+    group sizes 1..4, ragged query and key lengths (no multiple of 64
+    required), every rank, causal offsets that put the diagonal anywhere in
+    the visit order, bf16 and fp32 inputs and outputs."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        hq = hkv * int(rng.integers(1, 5))
+        nch = int(rng.integers(1, 9))
+        skv = nch * int(rng.integers(8, 97))
+        sq = int(rng.integers(1, 400))
+        rank = int(rng.integers(0, nch))
+        causal = bool(rng.integers(0, 2))
+        q_pos0 = int(rng.integers(0, skv + 64)) if causal else 0
+        din = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+        dout = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        cases.append((1 + int(rng.integers(0, 2)), hq, hkv, sq, skv, nch, rank, causal, q_pos0,
+                      din, dout))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(24, seed=2026),
+                         ids=lambda c: "x".join(str(v) for v in c[:9]))
+def test_shifted_random_sweep(case):
+    b, hq, hkv, sq, skv, nch, rank, causal, q_pos0, din, dout = case
+    _say(f"sweep {case}")
+    q, k, v = gen_qkv(batch=b, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=din, device=DEV, seed=sq * 7 + skv)
+    o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=nch, rank=rank, causal=causal,
+                                      q_pos0=q_pos0, out_dtype=dout)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=causal, q_pos0=q_pos0)
+    assert _max_err(o, o_ref) <= max(TOL_O[din], TOL_O[dout])
+    _check_lse(lse, lse_ref)
+
+
+@pytest.mark.parametrize("main_tiles", [1, 2, 3, 4, 5])
+def test_short_main_walks(main_tiles):
+    """A workgroup whose unmasked walk holds 1..5 tiles: the tile copies that
+    run past the walk's end, the prefetched operands of the tile after the
+    last one and the hand-over to the masked loop all act at once."""
+    _say(f"short walk {main_tiles}")
+    sq = 256
+    skv = 64 * main_tiles + 256
+    q, k, v = gen_qkv(batch=1, heads_q=4, heads_kv=2, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=torch.bfloat16, device=DEV, seed=31 + main_tiles)
+    # Query rows sit at the end of the keys: every query sees the first
+    # 64 * main_tiles keys, and the last 256 form the causal diagonal band.
+    q_pos0 = skv - sq
+    for nch, rank in [(1, 0), (2, 1)]:
+        if skv % nch:
+            continue
+        o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=nch, rank=rank, causal=True,
+                                          q_pos0=q_pos0, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=True, q_pos0=q_pos0)
+        assert _max_err(o, o_ref) <= TOL_O[torch.bfloat16], (nch, rank)
+        _check_lse(lse, lse_ref)
