@@ -164,8 +164,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, workload: str, copy_
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The engine clock takes some 50 back-to-back launches of the default
+    # workload (~40 ms of load) to settle; the default warm-up covers that.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama3_8b_gqa_32k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -1,15 +1,20 @@
 // Fused shifted-chunk attention forward, bf16 inputs, for gfx950 (CDNA4).
 //
-// A workgroup owns 256 query rows of one (batch, query head): four waves, one
-// per SIMD, of 64 rows each (two 32-row query blocks).  It walks the KV
-// chunks in the rank-shifted order c_j = (j + rank) % J (the `shift`
-// primitive of CommIR, papers.lqhl.me summary "Mercury (SOSP 2025)", section
-// 核心方法), 64 keys per tile, and carries the online-softmax state in
-// registers across chunk boundaries.  Rescaling that state when a chunk
-// starts is exactly the log-sum-exp merge of the chunk's partial result, so
-// one launch computes what attn_chunk_fwd followed by lse_merge computes
-// chunk by chunk.  Chunk ranges that no query of the workgroup can see
-// (causal) are skipped without touching memory.
+// A work item is 256 query rows of one (batch, query head): four waves, one
+// per SIMD, of 64 rows each (two 32-row query blocks).  The grid has at most
+// one workgroup per CU, each working through a fixed list of items (see the
+// block -> item mapping in the kernel): the hardware hands out waiting
+// workgroups in bursts to whichever CUs are free, which pairs heavy causal
+// items with heavy ones; a fixed list pairs heavy with light.  An item
+// walks the KV chunks in the rank-shifted order c_j = (j + rank) % J (the
+// `shift` primitive of CommIR, papers.lqhl.me summary "Mercury (SOSP
+// 2025)", section 核心方法), 64 keys per tile, and carries the
+// online-softmax state in registers across chunk boundaries.  Rescaling
+// that state when a chunk starts is exactly the log-sum-exp merge of the
+// chunk's partial result, so one launch computes what attn_chunk_fwd
+// followed by lse_merge computes chunk by chunk.  Chunk ranges that no
+// query of the workgroup can see (causal) are skipped without touching
+// memory.
 //
 // Matrix cores (v_mfma_f32_32x32x16_bf16), per wave, query block qb and
 // 64-key tile:
@@ -40,7 +45,9 @@
 //   Q4: O += P V, tile j-1, keys 32-63 + exp of tile j, key block 0, qb 0
 // An exponential is rounded to bf16 and summed one half step after it is
 // issued, so that no vector op waits on a transcendental result; K and V
-// operands are read three steps ahead.  Scheduling barriers fix the order,
+// operands are read three steps ahead (the first V operands of Q3 in the
+// last steps of Q2, which is why the stop flag is read early in Q2).
+// Scheduling barriers fix the order,
 // and the loop is unrolled by the ring depth so that ring slots are
 // compile-time constants.
 
@@ -453,21 +460,35 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const int lq = lane & 31;
   const int hh = lane >> 5;
 
-  // Block -> work item.  The hardware deals consecutive blocks round-robin to
-  // the 8 XCDs; remap so that the work items sharing one KV head land on one
-  // XCD (its L2 then serves their common K/V tiles), and within a head give
-  // the heaviest (latest, for causal) query tiles out first.
-  const int total = (int)gridDim.x;
-  const int full = total - (total & 7);
+  // Blocks -> work items (b, kv head, query head of its group, query tile).
+  // The grid holds at most one block per CU; each block walks a list of
+  // items.  The hardware deals consecutive blocks round-robin to the 8 XCDs:
+  // when the KV heads split evenly, the blocks of XCD x share the items of
+  // KV heads x, x+8, ... (its L2 then serves their common K/V tiles).  A
+  // list runs KV head by KV head, each head's items heaviest (latest query
+  // tile, for causal) first, and is dealt to the blocks sharing it in rounds
+  // of alternating direction, so that heavy and light items pair up.
+  const int n_blocks = (int)gridDim.x;
   const int bid = (int)blockIdx.x;
-  const int w = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
-  const int qt = p.num_q_tiles - 1 - (w % p.num_q_tiles);
-  int rest = w / p.num_q_tiles;
-  const int g = rest % p.group;
-  rest /= p.group;
-  const int hk = rest % p.heads_kv;
-  const int b = rest / p.heads_kv;
+  const int nkv = p.batch * p.heads_kv;
+  const int per_head = p.group * p.num_q_tiles;
+  const bool by_xcd = (nkv & 7) == 0 && (n_blocks & 7) == 0;
+  const int lanes = by_xcd ? (n_blocks >> 3) : n_blocks;
+  const int lidx = by_xcd ? (bid >> 3) : bid;
+  const int xcd = by_xcd ? (bid & 7) : 0;
+  const int n_list = (by_xcd ? (nkv >> 3) : nkv) * per_head;
+  for (int round = 0;; ++round) {
+  const int item = round * lanes + ((round & 1) ? lanes - 1 - lidx : lidx);
+  if (item >= n_list) break;
+  const int kvi = (by_xcd ? xcd + 8 * (item / per_head) : item / per_head);
+  const int i_in = item % per_head;
+  const int qt = p.num_q_tiles - 1 - i_in / p.group;
+  const int g = i_in % p.group;
+  const int hk = kvi % p.heads_kv;
+  const int b = kvi / p.heads_kv;
   const int h = hk * p.group + g;
+  // Every wave is done with the previous item's LDS tiles and flags.
+  if (round > 0) __syncthreads();
 
   const int64_t q_start = (int64_t)qt * kBlockM;
   const int64_t q_rows_wg = min((int64_t)kBlockM, p.seq_q - q_start);
@@ -677,6 +698,9 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     // pair per half step; Q2 overwrites those scores).  Q2 (t >= 8): key
     // block 1, with the key-block-0 maxima and the copies of K tile j+3 and
     // V tile j+2 (one copy instruction per half step).
+    bf16x8 va[4];
+    uint32_t vaddr[4];
+    bool flag = false;
     bf16x8 ka[4];
     ka[0] = read_k(ktile, koff, 0 >> 3, 0 & 7);
     ka[1] = read_k(ktile, koff, 1 >> 3, 1 & 7);
@@ -724,6 +748,19 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       } else {
         if (t == 8) store_pair(pe0, pe1, pb[1][3], 6, rh[1]);
         copy_step(2 * (t - 8));
+        if (t == 9) {
+          // Stop flag of tile j-1 and the V^T read addresses of its P V
+          // (the zero tile when stopping or before the first tile).
+          const int f_prev = (slot & 1) ? (int)(uint32_t)both : (int)(uint32_t)(both >> 32);
+          flag = __builtin_amdgcn_readfirstlane(f_prev) != 0;
+          const __bf16* vtile =
+              (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            vaddr[db] = lds_address(vtile) + (uint32_t)voff[db];
+            asm volatile("" : "+v"(vaddr[db]));
+          }
+        }
         // qb 0's key-block-0 scores were last written in half step 7A; the
         // first read waits for two full steps.
         if (t >= 10) max_pair(0, t - 10);
@@ -743,33 +780,20 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         copy_step(2 * (t - 8) + 1);
         if (t >= 11) max_pair(1, t - 11);
         if (t >= 13) max_pair(1, t - 8);
+        // The first V^T operands of Q3, three steps ahead (ka[(t+3)%4] is
+        // no longer read from t = 13 on).
+        if (t >= 13) {
+          const int n = t - 13;
+          va[n] = read_v_at(vaddr[n & 3], n >> 2);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int f_prev = (slot & 1) ? (int)(uint32_t)both : (int)(uint32_t)(both >> 32);
-    const bool flag = __builtin_amdgcn_readfirstlane(f_prev) != 0;
-    const __bf16* vtile =
-        (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
-    // Tile j-1 is committed (unless stopping): its sums join the row sums.
-    l_run[0] += flag ? 0.f : rs_pend[0] + rh[0];
-    l_run[1] += flag ? 0.f : rs_pend[1] + rh[1];
-    asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
     // ---- Q3, Q4: O += P V of tile j-1 (step st: keys 16*(st/4).., d
     // block st%4) ------------------------------------------------------
     //  Q3: max of key block 1 (then the reference); exp of tile j, key
     //      block 0, qb 1 (into pn: pb[1][0..1] is still being read).
     //  Q4: exp of tile j, key block 0, qb 0.
-    // This lane's V^T read addresses for the four d blocks of this tile.
-    uint32_t vaddr[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      vaddr[db] = lds_address(vtile) + (uint32_t)voff[db];
-      asm volatile("" : "+v"(vaddr[db]));
-    }
-    bf16x8 va[4];
-    va[0] = read_v_at(vaddr[0 & 3], 0 >> 2);
-    va[1] = read_v_at(vaddr[1 & 3], 1 >> 2);
-    va[2] = read_v_at(vaddr[2 & 3], 2 >> 2);
     // Key-block-1 maxima: qb 0 first (its scores were final 8 ops before the
     // end of Q2), qb 1 from the fifth half step on (its last op then lies
     // four matrix ops and their vector work back).
@@ -796,6 +820,12 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
       scale_max_kb1(2 * st + 1);
+      if (st == 0) {
+        // Tile j-1 is committed (unless stopping): its sums join the row sums.
+        l_run[0] += flag ? 0.f : rs_pend[0] + rh[0];
+        l_run[1] += flag ? 0.f : rs_pend[1] + rh[1];
+        asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // Common case: no lane's partial max exceeds its row's threshold.
@@ -1034,12 +1064,29 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       if (hh == 0) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
     }
   }
+  }  // items
+}
+
+// Compute units of the current device (one resident block each).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <typename TOut>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.num_q_tiles * p.batch * p.heads_q;
-  if (blocks == 0) return hipSuccess;
+  const int64_t items = (int64_t)p.num_q_tiles * p.batch * p.heads_q;
+  if (items == 0) return hipSuccess;
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const int64_t blocks = std::min<int64_t>(items, cus);
   FwdParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel((const void*)&attn_fwd_bf16_kernel<TOut>, dim3((unsigned)blocks),
