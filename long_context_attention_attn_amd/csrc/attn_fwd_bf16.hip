@@ -46,10 +46,8 @@
 // An exponential is rounded to bf16 and summed one half step after it is
 // issued, so that no vector op waits on a transcendental result; K and V
 // operands are read three steps ahead (the first V operands of Q3 in the
-// last steps of Q2, which is why the stop flag is read early in Q2).
-// Scheduling barriers fix the order,
-// and the loop is unrolled by the ring depth so that ring slots are
-// compile-time constants.
+// last steps of Q2).  Scheduling barriers fix the order, and the loop is
+// unrolled by the ring depth so that ring slots are compile-time constants.
 
 // K and V tiles stream straight from global memory into a 4-deep LDS ring
 // per tensor (global_load_lds_dwordx4, no registers involved): each wave
@@ -69,15 +67,15 @@
 // same way in any order, so taking those tiles last changes only rounding.
 //
 // Reference max.  Exponentials use a per-row reference m_ref, set by the
-// first tile and left alone in the hot loop: O and the row sums stay
-// multiples of the same exp2(-m_ref), so nothing is ever rescaled there (O
-// is modified only by matrix-core ops inside the loop; any other write to
-// it makes the compiler keep extra copies of it).  A score more than 64
-// (log2 units) above the reference would let p exceed 2^64; real data does
-// not do that, but if a tile does, the wave raises a workgroup flag before
-// that tile's P V, every wave then feeds the tile's P to an all-zero V tile
-// and drops its sums, and the masked loop redoes the walk from that tile,
-// where the reference moves per tile with an explicit rescale of O and l.
+// first tile and left alone in the hot loop while no score exceeds it by
+// more than 64 (log2 units): p then stays below 2^64, and O and the row
+// sums stay multiples of the same exp2(-m_ref), so the common path never
+// rescales (O is modified only by matrix-core ops there).  A tile with a
+// score beyond that (rare even in data with outlier keys) moves its rows'
+// reference up to the tile max, in a branch: the tile's scores are shifted,
+// the row sums shrink by exp2(old - new) at once and O at the end of the
+// tile, after the previous tile's P V (computed in the old scale) is in.
+// Each wave does this for its own rows, without waiting for the others.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -167,8 +165,8 @@ __device__ __forceinline__ void wait_copies(int n) {
 // Workgroup barrier without the release fence __syncthreads() adds: that
 // fence would wait for every global->LDS copy in flight, including the
 // prefetches of later tiles.  Copies a barrier must publish are waited for
-// explicitly with wait_copies().  The wave's own LDS operations (reads, and
-// the stop flag's store) are complete before it arrives.
+// explicitly with wait_copies().  The wave's own LDS reads are complete
+// before it arrives.
 __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -304,15 +302,11 @@ __device__ __forceinline__ bf16x8 read_v_at(uint32_t addr, int ks) {
   return a;
 }
 
-__device__ __forceinline__ bf16x8 read_v(const __bf16* vtile, const int (&voff)[4], int ks,
+// The same read for any V tile: vrel is the tile's LDS address minus that
+// of V ring slot 0 (wrapping), vaddr0[db] this lane's address in slot 0.
+__device__ __forceinline__ bf16x8 read_v(uint32_t vrel, const uint32_t (&vaddr0)[4], int ks,
                                          int db) {
-  const char* src = (const char*)vtile + voff[db] + ks * 4096;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 2048));
-  bf16x8 a;
-  a.lo = __builtin_bit_cast(bf16x4, lo);
-  a.hi = __builtin_bit_cast(bf16x4, hi);
-  return a;
+  return read_v_at(vaddr0[db] + vrel, ks);
 }
 
 // S^T += K Q^T for one 16-deep d step, Q^T taken from AGPRs (qk_mfma0: the
@@ -447,12 +441,6 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // the tile (P known to be zero), so that non-finite values in a V tile no
   // query of the wave can see never reach it through 0 * NaN.
   __shared__ __attribute__((aligned(16))) __bf16 lds_vzero[kTile];
-  // Set by a wave whose scores outgrow the reference: all waves stop the
-  // main walk.  Tile j writes flag[j & 1], tile j+1 reads it after the
-  // barrier between them; a wave can write that flag again only in tile
-  // j+2, after the barrier that every wave reaches once it has read it, so
-  // all waves read the same value (and stop after the same tile).
-  __shared__ __attribute__((aligned(8))) int lds_flag[2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in [0, 4)
@@ -487,7 +475,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const int hk = kvi % p.heads_kv;
   const int b = kvi / p.heads_kv;
   const int h = hk * p.group + g;
-  // Every wave is done with the previous item's LDS tiles and flags.
+  // Every wave is done with the previous item's LDS tiles.
   if (round > 0) __syncthreads();
 
   const int64_t q_start = (int64_t)qt * kBlockM;
@@ -585,7 +573,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   }
 
   // Per-lane LDS byte offsets of the matrix-core operands (see read_k, read_v).
-  int koff[8], voff[4];
+  int koff[8];
+  uint32_t voff[4];  // V^T reads: this lane's LDS byte address in V ring slot 0
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) koff[kk] = lq * 256 + (((2 * kk + hh) ^ (lq & 15)) * 16);
   {
@@ -593,13 +582,19 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     const int row = 4 * hh + t;  // row & 3 == t
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      voff[db] = row * 256 + (((db * 4 + 2 * gq + (u >> 1)) ^ (4 * t)) * 16) + (u & 1) * 8;
+      voff[db] = lds_address(&lds_v[0][0]) +
+                 (uint32_t)(row * 256 + (((db * 4 + 2 * gq + (u >> 1)) ^ (4 * t)) * 16) + (u & 1) * 8);
   }
 
   const float c = p.scale_log2;
   {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < kTile / 8; i += kThreads) *(u32x4*)(lds_vzero + 8 * i) = zero;
+    for (int i = tid; i < kTile / 8; i += kThreads) {
+      *(u32x4*)(lds_vzero + 8 * i) = zero;
+      // The main walk's first tile multiplies P = 0 into V ring slot 3 (the
+      // slot of "tile -1"), which no copy writes before tile 1.
+      *(u32x4*)(&lds_v[kRing - 1][0] + 8 * i) = zero;
+    }
   }
   f32x16 o[2][4];
   float m_ref[2], m_use[2];  // reference max; m_use = m_ref, or 0 while it is -inf
@@ -632,10 +627,6 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][qb][r] = -INFINITY;
   }
-  if (tid == 0) {
-    __atomic_store_n(&lds_flag[0], 0, __ATOMIC_RELAXED);
-    __atomic_store_n(&lds_flag[1], 0, __ATOMIC_RELAXED);
-  }
   // The compiler must not know P's starting value: a known constant gets
   // rebuilt by vector moves right in front of the asm matrix ops, which do
   // not see the wait states such a move needs before a matrix-core read.
@@ -659,10 +650,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   __syncthreads();
 
   int slot = 0;
-  bool dead_prev = true;  // P[j-1] is all zeros (before the first tile)
   float rs_pend[2] = {0.f, 0.f};  // key-block-0 sums of tile j-1
   int it = 0;
-  int stopped_at = n_tiles;  // iteration whose start saw a request to stop
+  // Per-row factor that tile j's far-score branch leaves for O (tile j-1's
+  // P V, still running then, completes in the old scale).
+  float o_scale[2] = {1.f, 1.f};
   // Sources of the next K and V tile copies (tiles it+3 and it+2, clamped to
   // the last tile), advanced by one tile per iteration.
   auto main_tile_src = [&](const __bf16* base, int64_t ss, int i) {
@@ -672,11 +664,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const __bf16* k_next = main_tile_src(kbase, p.k_ss, max(k_next_i, 0));
   const __bf16* v_next = main_tile_src(vbase, p.v_ss, max(v_next_i, 0));
   const int64_t k_tile_step = (int64_t)kN * p.k_ss, v_tile_step = (int64_t)kN * p.v_ss;
-  // The hot loop's body for a tile whose ring slot (its index mod 4, and so
-  // the parity of its stop flag) is a compile-time constant: every LDS
-  // address below is then a register plus an immediate.  Returns true when
-  // the walk stops after this tile.
-  auto tile_body = [&](auto slot_c) -> bool {
+  // The hot loop's body for a tile whose ring slot (its index mod 4) is a
+  // compile-time constant: every LDS address below is then a register plus
+  // an immediate.
+  auto tile_body = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
     // This tile copies K tile j+3 and V tile j+2 (main-walk tiles are full:
     // no row clamping).  Past the end of the walk the last tile is copied
@@ -686,9 +677,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     const uint32_t kdst = k_ring + (uint32_t)((slot + 3) & (kRing - 1)) * kTileBytes;
     const uint32_t vdst = v_ring + (uint32_t)((slot + 2) & (kRing - 1)) * kTileBytes;
     const __bf16* ktile = &lds_k[slot][0];
-    // Set by a wave at tile j-1 (before the last barrier): tile j-1's P V
-    // then reads the zero tile, its sums are dropped, and the walk stops
-    // after this tile; the rest loop redoes it from tile j-1.
+    // Tile j-1's V^T: slot 0's read addresses plus a constant (it goes into
+    // the instruction offset).
+    constexpr uint32_t v_slot_off = (uint32_t)((slot + kRing - 1) & (kRing - 1)) * kTileBytes;
+    bool rescale = false;  // a far score in this tile: O gets o_scale at its end
     float rh[2] = {0.f, 0.f};  // sums of tile j-1, key block 1
     float mx[2] = {-INFINITY, -INFINITY};
 
@@ -699,16 +691,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     // block 1, with the key-block-0 maxima and the copies of K tile j+3 and
     // V tile j+2 (one copy instruction per half step).
     bf16x8 va[4];
-    uint32_t vaddr[4];
-    bool flag = false;
     bf16x8 ka[4];
     ka[0] = read_k(ktile, koff, 0 >> 3, 0 & 7);
     ka[1] = read_k(ktile, koff, 1 >> 3, 1 & 7);
     ka[2] = read_k(ktile, koff, 2 >> 3, 2 & 7);
-    // Both flags in one read at a fixed address (behind the first K reads;
-    // first used after Q2, so its latency is hidden).  Only this tile's
-    // writes could race with the read, and they go to the other word.
-    const uint64_t both = __atomic_load_n((const uint64_t*)&lds_flag[0], __ATOMIC_RELAXED);
     float pe0 = 0.f, pe1 = 0.f;  // exponentials issued, not yet rounded and summed
     auto copy_step = [&](int h) {  // h = 0..15: K copies 0..3, then V copies 0..3
       if (h < 8) {
@@ -748,19 +734,6 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       } else {
         if (t == 8) store_pair(pe0, pe1, pb[1][3], 6, rh[1]);
         copy_step(2 * (t - 8));
-        if (t == 9) {
-          // Stop flag of tile j-1 and the V^T read addresses of its P V
-          // (the zero tile when stopping or before the first tile).
-          const int f_prev = (slot & 1) ? (int)(uint32_t)both : (int)(uint32_t)(both >> 32);
-          flag = __builtin_amdgcn_readfirstlane(f_prev) != 0;
-          const __bf16* vtile =
-              (dead_prev || flag) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            vaddr[db] = lds_address(vtile) + (uint32_t)voff[db];
-            asm volatile("" : "+v"(vaddr[db]));
-          }
-        }
         // qb 0's key-block-0 scores were last written in half step 7A; the
         // first read waits for two full steps.
         if (t >= 10) max_pair(0, t - 10);
@@ -784,7 +757,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         // no longer read from t = 13 on).
         if (t >= 13) {
           const int n = t - 13;
-          va[n] = read_v_at(vaddr[n & 3], n >> 2);
+          va[n] = read_v_at(voff[n & 3] + v_slot_off, n >> 2);
         }
       }
     }
@@ -814,16 +787,16 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     for (int st = 0; st < 6; ++st) {
       __builtin_amdgcn_sched_barrier(0);
       const int n = st + 3;
-      va[n % 4] = read_v_at(vaddr[n & 3], n >> 2);
+      va[n % 4] = read_v_at(voff[n & 3] + v_slot_off, n >> 2);
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
       scale_max_kb1(2 * st);
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
       scale_max_kb1(2 * st + 1);
       if (st == 0) {
-        // Tile j-1 is committed (unless stopping): its sums join the row sums.
-        l_run[0] += flag ? 0.f : rs_pend[0] + rh[0];
-        l_run[1] += flag ? 0.f : rs_pend[1] + rh[1];
+        // Tile j-1's sums join the row sums.
+        l_run[0] += rs_pend[0] + rh[0];
+        l_run[1] += rs_pend[1] + rh[1];
         asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
       }
     }
@@ -835,15 +808,16 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       for (int qb = 0; qb < 2; ++qb) {
         const float m_old = m_use[qb];
         const float m_tile = lane_swap32_max(mx[qb]) + m_old;  // max of s*c
-        // No reference yet (the first tile): set it, nothing to rescale.
+        // No reference yet (the first tile): set it, nothing to rescale (O
+        // and the row sums are zero).  A far score: the row's reference
+        // moves up to it; the row sums so far (through tile j-1) shrink by
+        // exp2(old - new) now, O once tile j-1's P V is in (end of tile).
         const bool first = m_ref[qb] == -INFINITY;
         const bool far_q = !first && m_tile > m_ref[qb] + kRescaleSlack;
-        m_ref[qb] = first ? m_tile : m_ref[qb];
-        // A far tile is thrown away; this keeps its probabilities (and
-        // those of the tiles up to the stop) at most 1, so that the zero V
-        // tile turns them into exact zeros.
-        m_use[qb] = first ? (m_tile == -INFINITY ? 0.f : m_tile)
-                          : (far_q ? fmaxf(m_use[qb], m_tile) : m_use[qb]);
+        o_scale[qb] = far_q ? exp2_fast(m_ref[qb] - m_tile) : 1.f;
+        l_run[qb] *= o_scale[qb];
+        m_ref[qb] = (first || far_q) ? m_tile : m_ref[qb];
+        m_use[qb] = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
         t_far[qb] = m_ref[qb] + kRescaleSlack - m_use[qb];
         // The tile's scores were shifted by the old m_use: shift them to the
         // new one.
@@ -855,8 +829,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         }
         far = far || far_q;
       }
-      if (__builtin_amdgcn_ballot_w64(far) != 0 && lane == 0)
-        __atomic_store_n(&lds_flag[slot & 1], 1, __ATOMIC_RELAXED);
+      rescale = __builtin_amdgcn_ballot_w64(far) != 0;
     }
     bf16x8 pn[2];  // P of tile j, key block 0, qb 1
     rs_pend[0] = 0.f;
@@ -885,7 +858,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (st + 3 < 16) {
         const int n = st + 3;
-        va[n % 4] = read_v_at(vaddr[n & 3], n >> 2);
+        va[n % 4] = read_v_at(voff[n & 3] + v_slot_off, n >> 2);
       }
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
       exp_job(2 * st);
@@ -896,7 +869,14 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     pb[1][0] = pn[0];
     pb[1][1] = pn[1];
-    dead_prev = false;
+    if (rescale) {
+      // Rare: tile j-1's P V (old scale) is complete once its ops retire.
+      matrix_settle();
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], agpr_get(o[qb][db]) * o_scale[qb]);
+    }
     {
       const bool kmore = k_next_i + 1 < n_tiles, vmore = v_next_i + 1 < n_tiles;
       k_next_i += kmore ? 1 : 0;
@@ -913,37 +893,25 @@ void attn_fwd_bf16_kernel(FwdParams p) {
                  :
                  : "memory");
     tile_barrier();
-    if (flag) {
-      stopped_at = it;
-      return true;
-    }
-    return false;
   };
   while (it < n_tiles) {
-    if (tile_body(SlotC<0>())) break;
+    tile_body(SlotC<0>());
     if (++it >= n_tiles) break;
-    if (tile_body(SlotC<1>())) break;
+    tile_body(SlotC<1>());
     if (++it >= n_tiles) break;
-    if (tile_body(SlotC<2>())) break;
+    tile_body(SlotC<2>());
     if (++it >= n_tiles) break;
-    if (tile_body(SlotC<3>())) break;
+    tile_body(SlotC<3>());
     ++it;
   }
-  // The slot after the last tile run (a stop at tile `it` ran it too).
-  slot = (stopped_at < n_tiles ? stopped_at + 1 : n_tiles) & (kRing - 1);
-  // Stopped early, or asked to stop at the last tile: the rest loop takes
-  // over from the tile that asked.
+  // The slot after the last tile.
+  slot = n_tiles & (kRing - 1);
   wait_copies(0);
-  // The last tile's flag (flag[1] is never written when there is no tile).
-  const bool late = __atomic_load_n(&lds_flag[(n_tiles + 1) & 1], __ATOMIC_RELAXED) != 0;
-  const bool stop = stopped_at < n_tiles || late;
-  const int resume = stopped_at < n_tiles ? stopped_at - 1 : (late ? n_tiles - 1 : n_tiles);
 
-  // The last tile of the main walk (unless stopped): its key-block-1
-  // probabilities, then its P V (its V sits in the slot before `slot`).
+  // The last tile of the main walk: its key-block-1 probabilities, then its
+  // P V (its V sits in the slot before `slot`; with no main walk at all P
+  // is zero and that slot is the zeroed slot 3).
   {
-    // After a stop the pending tile is redone below: its P (finite) meets
-    // the zero V tile and its sums are dropped.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float rh = 0.f;
@@ -951,33 +919,23 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       for (int i = 0; i < 8; ++i)
         store_pair(exp_s(s[1][qb], 2 * i), exp_s(s[1][qb], 2 * i + 1), pb[qb][2 + (i >> 2)],
                    (2 * i) & 7, rh);
-      l_run[qb] += stop ? 0.f : rs_pend[qb] + rh;
+      l_run[qb] += rs_pend[qb] + rh;
     }
-    const __bf16* vtile =
-        (dead_prev || stop) ? lds_vzero : &lds_v[(slot + kRing - 1) & (kRing - 1)][0];
+    const uint32_t vrel = (uint32_t)((slot + kRing - 1) & (kRing - 1)) * kTileBytes;
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 va = read_v(vtile, voff, st >> 2, st & 3);
+      const bf16x8 va = read_v(vrel, voff, st >> 2, st & 3);
       pv_mfma(o[0][st & 3], va, pb[0][st >> 2]);
       pv_mfma(o[1][st & 3], va, pb[1][st >> 2]);
     }
   }
 
   // ---- The rest, one tile at a time in slot 0, with masking and a per-row
-  // move of the reference: main-walk tiles from `resume` on (none unless
-  // stopped), then the causal diagonal band and ragged ends.
-  const int n_main_rest = n_tiles - resume;
-  for (int xt = 0; xt < n_main_rest + rest_walk.n; ++xt) {
-    const bool from_main = xt < n_main_rest;
-    Walk wk;
-    wk.a0 = from_main ? walk.a0 : rest_walk.a0;
-    wk.a_end = from_main ? walk.a_end : rest_walk.a_end;
-    wk.b0 = from_main ? walk.b0 : rest_walk.b0;
-    wk.b_end = from_main ? walk.b_end : rest_walk.b_end;
-    wk.n_a = from_main ? walk.n_a : rest_walk.n_a;
-    wk.n = from_main ? walk.n : rest_walk.n;
-    const int wi = xt < n_main_rest ? resume + xt : xt - n_main_rest;
+  // move of the reference: the causal diagonal band and ragged ends.
+  for (int xt = 0; xt < rest_walk.n; ++xt) {
+    const Walk& wk = rest_walk;
+    const int wi = xt;
     int t0, t_end;
     tile_bounds(wk, wi, t0, t_end);
     tile_barrier();  // every wave is done with the previous tile's LDS
@@ -1027,12 +985,12 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       l_run[qb] += rsum;
     }
     // P V; a wave none of whose queries sees the tile reads the zero tile.
-    const __bf16* vtile = dead ? lds_vzero : &lds_v[0][0];
+    const uint32_t vrel = lds_address(dead ? lds_vzero : &lds_v[0][0]) - lds_address(&lds_v[0][0]);
     matrix_settle();
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 va = read_v(vtile, voff, st >> 2, st & 3);
+      const bf16x8 va = read_v(vrel, voff, st >> 2, st & 3);
       pv_mfma(o[0][st & 3], va, pb[0][st >> 2]);
       pv_mfma(o[1][st & 3], va, pb[1][st >> 2]);
     }
