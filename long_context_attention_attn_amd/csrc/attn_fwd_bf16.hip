@@ -228,6 +228,10 @@ __device__ __forceinline__ void copy_one(uint32_t lds_addr, const __bf16* gbase,
 __device__ __forceinline__ void set_m0(uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0" : : "s"(lds_addr) : "m0");
 }
+// M0 = base + off, off a constant once the caller is unrolled.
+__device__ __forceinline__ void set_m0_add(uint32_t base, uint32_t off) {
+  asm volatile("s_add_u32 m0, %0, %1" : : "s"(base), "i"(off) : "m0");
+}
 __device__ __forceinline__ void copy_at_m0(const __bf16* gbase, uint32_t off) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(gbase) : "memory");
 }
@@ -655,15 +659,12 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // Per-row factor that tile j's far-score branch leaves for O (tile j-1's
   // P V, still running then, completes in the old scale).
   float o_scale[2] = {1.f, 1.f};
-  // Sources of the next K and V tile copies (tiles it+3 and it+2, clamped to
-  // the last tile), advanced by one tile per iteration.
-  auto main_tile_src = [&](const __bf16* base, int64_t ss, int i) {
-    return base + (int64_t)(i < walk.n_a ? walk.a0 + kN * i : kN * (i - walk.n_a)) * ss;
-  };
-  int k_next_i = min(3, n_tiles - 1), v_next_i = min(2, n_tiles - 1);
-  const __bf16* k_next = main_tile_src(kbase, p.k_ss, max(k_next_i, 0));
-  const __bf16* v_next = main_tile_src(vbase, p.v_ss, max(v_next_i, 0));
-  const int64_t k_tile_step = (int64_t)kN * p.k_ss, v_tile_step = (int64_t)kN * p.v_ss;
+  // First key rows of the next copies: K takes tile it+3, V tile it+2, both
+  // clamped to the last tile; V's row is the one K took a tile earlier.
+  auto main_row = [&](int i) { return i < walk.n_a ? walk.a0 + kN * i : kN * (i - walk.n_a); };
+  int k_i = min(3, n_tiles - 1);
+  int k_row = main_row(max(k_i, 0));
+  int v_row = main_row(max(min(2, n_tiles - 1), 0));
   // The hot loop's body for a tile whose ring slot (its index mod 4) is a
   // compile-time constant: every LDS address below is then a register plus
   // an immediate.
@@ -672,10 +673,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     // This tile copies K tile j+3 and V tile j+2 (main-walk tiles are full:
     // no row clamping).  Past the end of the walk the last tile is copied
     // again, into a ring slot no later read uses.
-    const __bf16* ksrc = k_next;
-    const __bf16* vsrc = v_next;
-    const uint32_t kdst = k_ring + (uint32_t)((slot + 3) & (kRing - 1)) * kTileBytes;
-    const uint32_t vdst = v_ring + (uint32_t)((slot + 2) & (kRing - 1)) * kTileBytes;
+    const __bf16* ksrc =
+        uniform_ptr((const __bf16*)((const char*)kbase + (uint64_t)(uint32_t)k_row * k_stride_b));
+    const __bf16* vsrc =
+        uniform_ptr((const __bf16*)((const char*)vbase + (uint64_t)(uint32_t)v_row * v_stride_b));
     const __bf16* ktile = &lds_k[slot][0];
     // Tile j-1's V^T: slot 0's read addresses plus a constant (it goes into
     // the instruction offset).
@@ -698,10 +699,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     float pe0 = 0.f, pe1 = 0.f;  // exponentials issued, not yet rounded and summed
     auto copy_step = [&](int h) {  // h = 0..15: K copies 0..3, then V copies 0..3
       if (h < 8) {
-        if (!(h & 1)) set_m0(kdst + 1024u * (h >> 1));
+        if (!(h & 1)) set_m0_add(k_ring, (uint32_t)((slot + 3) & (kRing - 1)) * kTileBytes + 1024u * (h >> 1));
         else copy_at_m0(ksrc, cl.k_off[h >> 1]);
       } else {
-        if (!(h & 1)) set_m0(vdst + 1024u * ((h - 8) >> 1));
+        if (!(h & 1)) set_m0_add(v_ring, (uint32_t)((slot + 2) & (kRing - 1)) * kTileBytes + 1024u * ((h - 8) >> 1));
         else copy_at_m0(vsrc, cl.v_offn[(h - 8) >> 1]);
       }
     };
@@ -720,6 +721,9 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         const int u = t + 3;
         ka[u % 4] = read_k(ktile, koff, u >> 3, u & 7);
       }
+      // One LDS wait per two steps: step t (even) also waits for step t+1's
+      // operand (read a step later than its own).
+      if (!(t & 1)) asm volatile("" : : "v"(ka[(t + 1) % 4]));
       if (kk == 0) qk_mfma0(s[kb][0], ka[t % 4], qv[0][kk]);
       else qk_mfma(s[kb][0], ka[t % 4], qv[0][kk]);
       if (t < 8) {
@@ -788,6 +792,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       const int n = st + 3;
       va[n % 4] = read_v_at(voff[n & 3] + v_slot_off, n >> 2);
+      if (!(st & 1)) asm volatile("" : : "v"(va[(st + 1) % 4]));
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
       scale_max_kb1(2 * st);
       __builtin_amdgcn_sched_barrier(0);
@@ -860,6 +865,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         const int n = st + 3;
         va[n % 4] = read_v_at(voff[n & 3] + v_slot_off, n >> 2);
       }
+      if (!(st & 1)) asm volatile("" : : "v"(va[(st + 1) % 4]));
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
       exp_job(2 * st);
       __builtin_amdgcn_sched_barrier(0);
@@ -878,11 +884,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], agpr_get(o[qb][db]) * o_scale[qb]);
     }
     {
-      const bool kmore = k_next_i + 1 < n_tiles, vmore = v_next_i + 1 < n_tiles;
-      k_next_i += kmore ? 1 : 0;
-      v_next_i += vmore ? 1 : 0;
-      k_next = uniform_ptr(!kmore ? k_next : (k_next_i == walk.n_a ? kbase : k_next + k_tile_step));
-      v_next = uniform_ptr(!vmore ? v_next : (v_next_i == walk.n_a ? vbase : v_next + v_tile_step));
+      v_row = k_row;
+      const int kn = k_i + 1;
+      const bool kmore = kn < n_tiles;
+      k_row = kmore ? (kn == walk.n_a ? 0 : k_row + kN) : k_row;
+      k_i = kmore ? kn : k_i;
     }
 
     // Copies still allowed in flight: those issued after K[j+1] and V[j],
@@ -907,6 +913,17 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // The slot after the last tile.
   slot = n_tiles & (kRing - 1);
   wait_copies(0);
+  // The rest tiles (below) continue the ring: rest tile r sits in slot
+  // (n_tiles + r) mod 4.  The first two are fetched now, under the last
+  // main tile's P V: no wave reads K any more (every wave passed the last
+  // tile's barrier), and that P V reads only the V slot before `slot`.
+  const int n_rest = rest_walk.n;
+  auto copy_rest = [&](int r) {
+    copy_tile_k(k_copy(rest_walk, r, (slot + r) & (kRing - 1)));
+    copy_tile_v(v_copy(rest_walk, r, (slot + r) & (kRing - 1)));
+  };
+  if (n_rest > 0) copy_rest(0);
+  if (n_rest > 1) copy_rest(1);
 
   // The last tile of the main walk: its key-block-1 probabilities, then its
   // P V (its V sits in the slot before `slot`; with no main walk at all P
@@ -931,19 +948,20 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  // ---- The rest, one tile at a time in slot 0, with masking and a per-row
-  // move of the reference: the causal diagonal band and ragged ends.
-  for (int xt = 0; xt < rest_walk.n; ++xt) {
-    const Walk& wk = rest_walk;
-    const int wi = xt;
+  // ---- The rest, one tile at a time, with masking: the causal diagonal
+  // band and ragged ends.  Two tiles ahead in flight.
+  for (int xt = 0; xt < n_rest; ++xt) {
     int t0, t_end;
-    tile_bounds(wk, wi, t0, t_end);
-    tile_barrier();  // every wave is done with the previous tile's LDS
-    copy_tile_k(k_copy(wk, wi, 0));
-    copy_tile_v(v_copy(wk, wi, 0));
-    wait_copies(0);
+    tile_bounds(rest_walk, xt, t0, t_end);
+    const int rslot = (slot + xt) & (kRing - 1);
+    // This wave's copies of tile xt are in (tile xt+1's may still fly) ...
+    if (xt + 1 < n_rest) wait_copies(8);
+    else wait_copies(0);
+    // ... and everyone's; every wave is done with tile xt-1, so tile xt+2
+    // may take the slot of tile xt-2.
     tile_barrier();
-    const __bf16* ktile = &lds_k[0][0];
+    if (xt + 2 < n_rest) copy_rest(xt + 2);
+    const __bf16* ktile = &lds_k[rslot][0];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       __builtin_amdgcn_sched_barrier(0);
@@ -967,16 +985,20 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mxq = vmax(vmax(mxq, s[0][qb][r]), s[1][qb][r]);
       const float m_tile = lane_swap32_max(mxq) * c;
-      const bool move = m_tile > m_ref[qb];
+      // The reference moves under the same rule as in the main walk (a
+      // row's first visible keys always move it: -inf + slack = -inf).
+      const bool move = m_tile > m_ref[qb] + kRescaleSlack;
       const float m_new = move ? m_tile : m_ref[qb];
       const float alpha = move ? exp2_fast(m_ref[qb] - m_new) : 1.f;
       m_ref[qb] = m_new;
       m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
       l_run[qb] *= alpha;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        __builtin_amdgcn_sched_barrier(0);
-        agpr_set(o[qb][db], agpr_get(o[qb][db]) * alpha);
+        for (int db = 0; db < 4; ++db) {
+          __builtin_amdgcn_sched_barrier(0);
+          agpr_set(o[qb][db], agpr_get(o[qb][db]) * alpha);
+        }
       }
       float rsum = 0.f;
 #pragma unroll
@@ -985,7 +1007,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       l_run[qb] += rsum;
     }
     // P V; a wave none of whose queries sees the tile reads the zero tile.
-    const uint32_t vrel = lds_address(dead ? lds_vzero : &lds_v[0][0]) - lds_address(&lds_v[0][0]);
+    const uint32_t vrel =
+        lds_address(dead ? lds_vzero : &lds_v[rslot][0]) - lds_address(&lds_v[0][0]);
     matrix_settle();
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
