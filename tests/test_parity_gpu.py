@@ -425,3 +425,35 @@ def test_short_main_walks(main_tiles):
         o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=True, q_pos0=q_pos0)
         assert _max_err(o, o_ref) <= TOL_O[torch.bfloat16], (nch, rank)
         _check_lse(lse, lse_ref)
+
+
+@pytest.mark.parametrize("hq,hkv,sq,causal", [
+    (12, 3, 23 * 256 - 100, True),   # KV heads not a multiple of 8: one list for all blocks
+    (16, 8, 17 * 256 - 100, True),   # a list per XCD, 34 items over 32 blocks
+    (16, 8, 17 * 256 - 100, False),
+])
+def test_more_work_items_than_workgroups(hq, hkv, sq, causal):
+    """More 256-row work items than the one-per-CU grid has workgroups (256
+    on MI355X): blocks walk their item lists over several rounds, the last
+    one partial.  The first and last row of every query tile of every head
+    are checked, so every item is."""
+    _say(f"item lists hq {hq} hkv {hkv} sq {sq} causal {causal}")
+    # Causal from position 0: the first four query tiles hold the diagonal,
+    # the later ones see every key (items of unequal work).
+    skv, nch, rank, q_pos0 = 1024, 4, 1, 0
+    q, k, v = gen_qkv(batch=1, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=torch.bfloat16, device=DEV, seed=hq * 100 + hkv)
+    o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=nch, rank=rank, causal=causal,
+                                      q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    rows = sorted(set(list(range(0, sq, 256)) + [min(t + 255, sq - 1) for t in range(0, sq, 256)]))
+    rows = np.array(rows, dtype=np.int64)
+    rows_t = torch.from_numpy(rows).to(o.device)
+    group = hq // hkv
+    for h in range(hq):
+        o_ref, lse_ref = oracle.attention_rows(q[0:1, h:h + 1].cpu(),
+                                               k[0:1, h // group:h // group + 1].cpu(),
+                                               v[0:1, h // group:h // group + 1].cpu(), 0, 0,
+                                               rows, causal=causal, q_pos0=q_pos0)
+        assert _max_err(o[0, h].index_select(0, rows_t), o_ref) <= TOL_O[torch.bfloat16], h
+        _check_lse(lse[0, h].index_select(0, rows_t), lse_ref)
