@@ -638,9 +638,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
                "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pb[1][2]), "+v"(pb[1][3]));
 
   // ---- Main walk.  The first tile sets each row's reference (nothing is
-  // accumulated yet).  A later score more than the slack above it (which
-  // real data does not produce) stops the walk for all waves before that
-  // tile's P V; the rest loop below then takes over from that tile.
+  // accumulated yet); a later tile with a score more than the slack above it
+  // moves the reference of the rows concerned (rare branch below).
   if (n_tiles > 0) {
     copy_tile_k(k_copy(walk, 0, 0));
     copy_tile_v(v_copy(walk, 0, 0));
