@@ -331,6 +331,11 @@ FAR_CASES = [
     ("diagonal_band", [(1856, 1920, 32.0)], None),
     ("two_jumps", [(768, 832, 32.0), (1088, 1152, 48.0)], None),
     ("one_wave_only", [(1088, 1152, 32.0)], (128, 192)),
+    # Only one 32-key half of a tile: the two halves are checked differently
+    # (key block 0 through its probability sums at the end of the tile).
+    ("key_block_0_only", [(768, 800, 32.0)], None),
+    ("key_block_1_only", [(800, 832, 32.0)], None),
+    ("last_tile_key_block_0", [(448, 480, 32.0)], None),
 ]
 
 
@@ -340,7 +345,8 @@ def test_scores_far_above_the_first_tile(case, din):
     """Keys whose scores lie ~130 (log2 units) above everything seen before
     them in visit order: the running reference has to move by far more than
     any working slack, mid-walk, at the walk's last full tile, inside the
-    causal diagonal band, twice, or for one 64-row group of queries only.
+    causal diagonal band, twice, for one 64-row group of queries only, or in
+    one 32-key half of a tile only.
     With C = 512 and rank 1 the visit order is rows 512..2047, then 0..511.
     The second jump adds 45 (raw score units) on top of the first; it is kept
     that small because an fp32 dot product of magnitude ~2000 already carries
