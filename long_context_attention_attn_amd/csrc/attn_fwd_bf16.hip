@@ -938,12 +938,15 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       l_run[qb] += rs_pend[qb] + rh;
     }
     const uint32_t vrel = (uint32_t)((slot + kRing - 1) & (kRing - 1)) * kTileBytes;
+    bf16x8 va[3];  // V operands two steps ahead
+    va[0] = read_v(vrel, voff, 0, 0);
+    va[1] = read_v(vrel, voff, 0, 1);
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 va = read_v(vrel, voff, st >> 2, st & 3);
-      pv_mfma(o[0][st & 3], va, pb[0][st >> 2]);
-      pv_mfma(o[1][st & 3], va, pb[1][st >> 2]);
+      if (st + 2 < 16) va[(st + 2) % 3] = read_v(vrel, voff, (st + 2) >> 2, (st + 2) & 3);
+      pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
+      pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
     }
   }
 
@@ -961,17 +964,23 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     tile_barrier();
     if (xt + 2 < n_rest) copy_rest(xt + 2);
     const __bf16* ktile = &lds_k[rslot][0];
+    {
+      // K operands two steps ahead.
+      bf16x8 ka[3];
+      ka[0] = read_k(ktile, koff, 0, 0);
+      ka[1] = read_k(ktile, koff, 0, 1);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int kb = t >> 3, kk = t & 7;
-      const bf16x8 ka = read_k(ktile, koff, kb, kk);
-      if (kk == 0) {
-        qk_mfma0(s[kb][0], ka, qv[0][kk]);
-        qk_mfma0(s[kb][1], ka, qv[1][kk]);
-      } else {
-        qk_mfma(s[kb][0], ka, qv[0][kk]);
-        qk_mfma(s[kb][1], ka, qv[1][kk]);
+      for (int t = 0; t < 16; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = t >> 3, kk = t & 7;
+        if (t + 2 < 16) ka[(t + 2) % 3] = read_k(ktile, koff, (t + 2) >> 3, (t + 2) & 7);
+        if (kk == 0) {
+          qk_mfma0(s[kb][0], ka[t % 3], qv[0][kk]);
+          qk_mfma0(s[kb][1], ka[t % 3], qv[1][kk]);
+        } else {
+          qk_mfma(s[kb][0], ka[t % 3], qv[0][kk]);
+          qk_mfma(s[kb][1], ka[t % 3], qv[1][kk]);
+        }
       }
     }
     matrix_settle();
@@ -1009,12 +1018,18 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     const uint32_t vrel =
         lds_address(dead ? lds_vzero : &lds_v[rslot][0]) - lds_address(&lds_v[0][0]);
     matrix_settle();
+    {
+      // V operands two steps ahead.
+      bf16x8 va[3];
+      va[0] = read_v(vrel, voff, 0, 0);
+      va[1] = read_v(vrel, voff, 0, 1);
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 va = read_v(vrel, voff, st >> 2, st & 3);
-      pv_mfma(o[0][st & 3], va, pb[0][st >> 2]);
-      pv_mfma(o[1][st & 3], va, pb[1][st >> 2]);
+      for (int st = 0; st < 16; ++st) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 2 < 16) va[(st + 2) % 3] = read_v(vrel, voff, (st + 2) >> 2, (st + 2) & 3);
+        pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
+        pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      }
     }
     matrix_settle();
   }
