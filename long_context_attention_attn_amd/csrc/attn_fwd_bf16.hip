@@ -1037,6 +1037,14 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   matrix_settle();
   // Finalise: O = acc / l, LSE = (m_ref + log2 l) ln 2; l == 0 means no
   // visible key (O = 0, LSE = -inf).  NaN in l propagates.
+  // bf16 output goes through LDS: each wave stages its 32-row blocks in its
+  // own 16 KiB of the K ring (every wave is past its last tile once the
+  // barrier below is passed), so that the stores write whole rows, 16 bytes
+  // per lane, instead of 8 bytes into each of 32 rows per instruction.
+  constexpr bool kStaged = sizeof(TOut) == 2;
+  constexpr int kStageRow = 128 * 2 + 16;  // bytes per staged row (head_dim 128, padded: spreads banks)
+  char* const stage = (char*)&lds_k[wave][0];
+  if (kStaged) tile_barrier();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = lane_swap32_add(l_run[qb]);
@@ -1044,7 +1052,29 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse = empty ? -INFINITY : (m_ref[qb] + __log2f(l_tot)) * 0.69314718055994530942f;
     const int64_t my_q = wave_q0 + 32 * qb + lq;
-    if (my_q < p.seq_q) {
+    if (kStaged) {
+      // This lane's values of row lq: columns db*32 + 8*gq + 4*hh .. +3.
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const f32x16 ov = agpr_get(o[qb][db]);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const bf16x4 x = {(__bf16)(ov[4 * gq] * inv), (__bf16)(ov[4 * gq + 1] * inv),
+                            (__bf16)(ov[4 * gq + 2] * inv), (__bf16)(ov[4 * gq + 3] * inv)};
+          *(bf16x4*)(stage + lq * kStageRow + (db * 32 + 8 * gq + 4 * hh) * 2) = x;
+        }
+      }
+      // Back by rows: row 4*i + lane/16, 16-byte chunk lane%16.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + (lane >> 4), chunk = lane & 15;
+        const u32x4 d = *(const u32x4*)(stage + row * kStageRow + chunk * 16);
+        const int64_t q = wave_q0 + 32 * qb + row;
+        if (q < p.seq_q)
+          *(u32x4*)((char*)p.o + (b * p.o_sb + h * p.o_sh + q * p.o_ss) * 2 + chunk * 16) = d;
+      }
+      if (hh == 0 && my_q < p.seq_q) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
+    } else if (my_q < p.seq_q) {
       TOut* orow = (TOut*)p.o + b * p.o_sb + h * p.o_sh + my_q * p.o_ss;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {

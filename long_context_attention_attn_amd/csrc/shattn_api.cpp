@@ -69,7 +69,9 @@ int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v
   if (!kv_empty && (k == nullptr || v == nullptr)) return SHATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SHATTN_EINVAL;
   if (((uintptr_t)lse & 3u) != 0) return SHATTN_EINVAL;
-  // Grid size: one workgroup per block_m query rows of each (batch, head).
+  // Work items: block_m query rows of each (batch, head) (the bf16 kernel
+  // walks them with at most one workgroup per CU, the fp32 kernel launches
+  // one workgroup per item).
   const int64_t bm = shattn::block_m((DType)d->in_dtype);
   const int64_t tiles = (d->seq_q + bm - 1) / bm;
   if (tiles * (int64_t)d->batch * d->heads_q > INT32_MAX) return SHATTN_EUNSUPPORTED;
