@@ -118,6 +118,19 @@ WORKLOADS = (
     Workload(4, "gqa_b16_128k_heavy", "bf16", 16, 32, 8, 128, 1024, 130048, 131072, 16, 15,
              True, heavy_frac=0.01, heavy_mult=8.0,
              summary="Batch-16 GQA, 128K KV in 16 chunks, rank 15, causal, 1% of K rows x8"),
+    # One GPU's share under two other schedules of the same attention.
+    # Head-sharded (Ulysses / USP): after the all-to-all each of 8 GPUs holds
+    # Hq/8 query heads and Hkv/8 KV heads over the whole sequence (GQA caps
+    # the split at Hkv ways), i.e. one chunk, rank 0, positions from 0.
+    Workload(5, "llama3_8b_ulysses_32k", "bf16", 1, 4, 1, 128, 32768, 0, 32768, 1, 0, True,
+             std=0.5,
+             summary="Llama-3-8B-like GQA, 32K context head-sharded over 8 GPUs: "
+                     "4 query heads, 1 KV head, whole sequence, causal"),
+    # The 2M-token end of the context sweep on 8 GPUs: rank 3's 256K-row Q
+    # shard against the 2M-row KV buffer in 8 chunks.
+    Workload(6, "llama3_8b_gqa_2m", "bf16", 1, 32, 8, 128, 262144, 3 * 262144, 2097152, 8, 3,
+             True, std=0.5,
+             summary="Llama-3-8B-like GQA, 2M-token context on 8 ranks, rank 3, causal"),
 )
 
 BY_NAME = {w.name: w for w in WORKLOADS}

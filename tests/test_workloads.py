@@ -33,11 +33,19 @@ def test_table_shapes():
         ("bf16", 16, 32, 32, 128, 4096, 16384, 4, 2, False),
         ("bf16", 1, 64, 8, 128, 2048, 524288, 64, 32, True),
         ("bf16", 16, 32, 8, 128, 1024, 131072, 16, 15, True),
+        ("bf16", 1, 4, 1, 128, 32768, 32768, 1, 0, True),
+        ("bf16", 1, 32, 8, 128, 262144, 2097152, 8, 3, True),
     ]
     # Q shards sit at rank * Sq on the global axis for the causal workloads.
     assert BY_NAME["llama3_8b_gqa_32k"].q_pos0 == 3 * 4096
     assert BY_NAME["llama3_70b_gqa_512k"].q_pos0 == 262144
     assert BY_NAME["gqa_b16_128k_heavy"].q_pos0 == 131072 - 1024
+    assert BY_NAME["llama3_8b_ulysses_32k"].q_pos0 == 0
+    assert BY_NAME["llama3_8b_gqa_2m"].q_pos0 == 3 * 262144
+    # Head-sharded 8 ways, the 32K model does 1/8 of the full causal attention
+    # of its 32 query heads per GPU.
+    w = BY_NAME["llama3_8b_ulysses_32k"]
+    assert w.flops() * 8 == 4 * 128 * 32 * (32768 * 32769 // 2)
     # Algorithmic flops of the headline workload (4 * D * B * Hq * pairs).
     assert BY_NAME["llama3_8b_gqa_32k"].flops() == 4 * 128 * 32 * 58_722_304
 
