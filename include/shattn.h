@@ -135,6 +135,49 @@ SHATTN_API int attn_shifted_fwd(const shattn_desc* desc, const void* q, const vo
                      int64_t kv_len_total, int32_t num_chunks, int32_t rank, void* o,
                      float* lse, hipStream_t stream);
 
+/*
+ * attn_shifted_fwd_overlapped — the chunk walk of attn_shifted_fwd with each
+ * chunk's K/V rows fetched while the chunks before it compute: the shifted
+ * schedule's overlap of the next chunk's transfer with local attention
+ * (Silicon & Systems digest of Mercury, section "The hidden cost of
+ * synchronized operators"; papers.lqhl.me summary, section 核心方法: remote
+ * chunks are moved when their consumer needs them).  On one GPU the source
+ * stands in for the peer that holds the chunk.
+ *
+ * k, v: the device KV buffers (whole length), which on entry hold the
+ * rank's own chunk, chunk `rank`.  k_src, v_src: where the other chunks'
+ * rows come from: pinned host memory (hipHostMalloc) or memory of another
+ * device, laid out with desc->k_stride / v_stride like k, v (sequence
+ * strides >= head_dim).  The own chunk is computed first, at once; for
+ * j = 1..J-1 and c = (j + rank) % num_chunks, the call enqueues on
+ * copy_stream the copy of chunk c's rows of every (batch, KV head) slice,
+ * and on compute_stream, behind an event on those copies, the partial of Q
+ * against chunk c (attn_chunk_fwd) merged into (o, lse) (lse_merge): the
+ * copy of each chunk runs while the chunks before it compute.  A causal
+ * chunk that starts after the last query's position is neither copied nor
+ * computed (its rows of k, v are left as they were).
+ *
+ * Outputs: o, fp32, contiguous [batch, heads_q, seq_q, head_dim] (so
+ * desc->o_stride must be the contiguous strides; desc->out_dtype is
+ * ignored), and lse, fp32 [batch, heads_q, seq_q].  o_part, lse_part: the
+ * caller's scratch of the same shapes for one chunk's partial.  None of the
+ * four may overlap.  Results equal attn_chunk_fwd over the visited chunks
+ * merged in visit order, which equals attn_shifted_fwd up to rounding.
+ *
+ * Streams: copy_stream first waits for the work already enqueued on
+ * compute_stream (which may still read k, v); compute_stream ends after all
+ * of the call's work.  The two streams must differ (two null streams are
+ * rejected).  The call creates and destroys HIP events; it allocates no
+ * memory and never synchronizes.  Arguments are checked before anything is
+ * enqueued; a HIP error while enqueuing returns SHATTN_EHIP, with the work
+ * enqueued before it left in the streams.
+ */
+SHATTN_API int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q,
+                                const void* k_src, const void* v_src, void* k, void* v,
+                                int64_t kv_len_total, int32_t num_chunks, int32_t rank,
+                                float* o, float* lse, float* o_part, float* lse_part,
+                                hipStream_t compute_stream, hipStream_t copy_stream);
+
 /* attn_status_string — static, NUL-terminated name of a status code. */
 SHATTN_API const char* attn_status_string(int status);
 

@@ -21,6 +21,7 @@ __all__ = [
     "attn_chunk_fwd",
     "lse_merge",
     "attn_shifted_fwd",
+    "attn_shifted_fwd_overlapped",
     "attn_status_string",
     "DTYPE_CODES",
 ]
@@ -84,6 +85,9 @@ def load_library():
     lib.lse_merge.restype = ctypes.c_int
     lib.attn_shifted_fwd.argtypes = [dp, vp, vp, vp, i64, i32, i32, vp, vp, vp]
     lib.attn_shifted_fwd.restype = ctypes.c_int
+    lib.attn_shifted_fwd_overlapped.argtypes = [dp, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp,
+                                                vp, vp, vp, vp]
+    lib.attn_shifted_fwd_overlapped.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -197,3 +201,43 @@ def attn_shifted_fwd(q, k, v, *, num_chunks: int, rank: int, causal: bool = Fals
                                          out.data_ptr(), lse.data_ptr(), _stream(q))
     _check("attn_shifted_fwd", st)
     return out, lse
+
+
+def attn_shifted_fwd_overlapped(q, k_src, v_src, k, v, *, num_chunks: int, rank: int,
+                                causal: bool = False, q_pos0: int = 0, scale=None,
+                                copy_stream=None):
+    """Shifted chunk walk with each chunk's K/V rows copied from ``k_src`` /
+    ``v_src`` (pinned host tensors, or another device's) into the device
+    tensors ``k`` / ``v`` on ``copy_stream`` while earlier chunks compute on
+    the current stream.
+
+    Returns (O float32, LSE float32).  ``copy_stream`` defaults to a new
+    stream of default priority.
+    """
+    _require_cuda(q, k, v)
+    for src, dst in ((k_src, k), (v_src, v)):
+        if src.shape != dst.shape or src.dtype != dst.dtype or src.stride() != dst.stride():
+            raise ValueError("source and device K/V tensors must match in shape and layout")
+        if not src.is_cuda and not src.is_pinned():
+            raise ValueError("a host source must be pinned memory")
+    b, hq, sq, dim = q.shape
+    if k.shape[2] != v.shape[2]:
+        raise ValueError("K and V differ in length")
+    o = torch.empty((b, hq, sq, dim), dtype=torch.float32, device=q.device)
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    o_part = torch.empty_like(o)
+    lse_part = torch.empty_like(lse)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=q.device)
+    desc = make_desc(q, k, v, o, causal=causal, q_pos0=q_pos0, scale=scale,
+                     out_dtype=torch.float32)
+    st = load_library().attn_shifted_fwd_overlapped(
+        ctypes.byref(desc), q.data_ptr(), k_src.data_ptr(), v_src.data_ptr(), k.data_ptr(),
+        v.data_ptr(), k.shape[2], int(num_chunks), int(rank), o.data_ptr(), lse.data_ptr(),
+        o_part.data_ptr(), lse_part.data_ptr(), _stream(q), copy_stream.cuda_stream)
+    _check("attn_shifted_fwd_overlapped", st)
+    # The sources must stay alive until the current stream has passed this
+    # call's work (the caller's references do that); the scratch and the
+    # device K/V are ordered by the current stream, which ends after the
+    # copies.
+    return o, lse

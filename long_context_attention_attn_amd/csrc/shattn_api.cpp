@@ -1,9 +1,10 @@
 // C-ABI entry points declared in include/shattn.h.
 //
 // Every argument is checked on the host before any HIP runtime call, so the
-// error paths need no GPU.  Each successful call enqueues exactly one kernel
-// on the caller's stream and returns the launch status; nothing synchronizes
-// and nothing is allocated.
+// error paths need no GPU.  Each successful kernel call enqueues exactly one
+// kernel on the caller's stream and returns the launch status; the
+// overlapped walk enqueues copies, events and those kernels on two streams.
+// Nothing synchronizes and no memory is allocated.
 
 #include <math.h>
 #include <stdint.h>
@@ -136,11 +137,13 @@ int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const 
   return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, DType::F32, stream));
 }
 
-int lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc, const float* o_part,
-              const float* lse_part, hipStream_t stream) {
-  if (rows < 0 || rows > kPosLimit) return SHATTN_EINVAL;
-  if (head_dim < 4 || head_dim > 256 || head_dim % 4 != 0) return SHATTN_EINVAL;
-  if (rows == 0) return SHATTN_OK;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of lse_merge for rows > 0.
+int check_merge(int64_t rows, int32_t head_dim, const float* o_acc, const float* lse_acc,
+                const float* o_part, const float* lse_part) {
   if (!o_acc || !lse_acc || !o_part || !lse_part) return SHATTN_EINVAL;
   if (!aligned16(o_acc) || !aligned16(o_part)) return SHATTN_EINVAL;
   if ((((uintptr_t)lse_acc) & 3u) || (((uintptr_t)lse_part) & 3u)) return SHATTN_EINVAL;
@@ -152,6 +155,20 @@ int lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc, cons
   if (oa < ob + obytes && ob < oa + obytes) return SHATTN_EINVAL;
   if (la < lb + lbytes && lb < la + lbytes) return SHATTN_EINVAL;
   if (oa < la + lbytes && la < oa + obytes) return SHATTN_EINVAL;
+  return SHATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc, const float* o_part,
+              const float* lse_part, hipStream_t stream) {
+  if (rows < 0 || rows > kPosLimit) return SHATTN_EINVAL;
+  if (head_dim < 4 || head_dim > 256 || head_dim % 4 != 0) return SHATTN_EINVAL;
+  if (rows == 0) return SHATTN_OK;
+  const int st = check_merge(rows, head_dim, o_acc, lse_acc, o_part, lse_part);
+  if (st != SHATTN_OK) return st;
   return status_of(
       shattn::launch_lse_merge(rows, head_dim, o_acc, lse_acc, o_part, lse_part, stream));
 }
@@ -177,6 +194,125 @@ int attn_shifted_fwd(const shattn_desc* desc, const void* q, const void* k, cons
   if (desc->batch == 0 || desc->seq_q == 0) return SHATTN_OK;
   return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, (DType)desc->out_dtype,
                                            stream));
+}
+
+int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q, const void* k_src,
+                                const void* v_src, void* k, void* v, int64_t kv_len_total,
+                                int32_t num_chunks, int32_t rank, float* o, float* lse,
+                                float* o_part, float* lse_part, hipStream_t compute_stream,
+                                hipStream_t copy_stream) {
+  if (num_chunks < 1 || rank < 0 || rank >= num_chunks) return SHATTN_EINVAL;
+  if (kv_len_total < 0 || kv_len_total > kPosLimit || kv_len_total % num_chunks != 0)
+    return SHATTN_EINVAL;
+  if (desc == nullptr) return SHATTN_EINVAL;
+  int st = check_desc(desc, q, k, v, o, lse, kv_len_total, 4);
+  if (st != SHATTN_OK) return st;
+  if (kv_len_total > kKvRowLimit) return SHATTN_EUNSUPPORTED;
+  if (compute_stream == copy_stream) return SHATTN_EINVAL;
+  const bool q_empty = desc->batch == 0 || desc->seq_q == 0;
+  const bool kv_empty = desc->batch == 0 || kv_len_total == 0;
+  if (!kv_empty && (k_src == nullptr || v_src == nullptr)) return SHATTN_EINVAL;
+  // Rows must not overlap: each chunk is copied row by row at most.
+  if (desc->k_stride[2] < desc->head_dim || desc->v_stride[2] < desc->head_dim)
+    return SHATTN_EINVAL;
+  // O and its partial are contiguous [B, Hq, Sq, D]: the merge runs over rows.
+  const int64_t dim = desc->head_dim;
+  const int64_t rows = (int64_t)desc->batch * desc->heads_q * desc->seq_q;
+  if (desc->o_stride[2] != dim || desc->o_stride[1] != desc->seq_q * dim ||
+      desc->o_stride[0] != desc->heads_q * desc->seq_q * dim)
+    return SHATTN_EINVAL;
+  if (q_empty) return SHATTN_OK;
+  st = check_merge(rows, (int32_t)dim, o, lse, o_part, lse_part);
+  if (st != SHATTN_OK) return st;
+  // The chunk partials are written too: no two of the four outputs overlap.
+  {
+    const uintptr_t ob = (uintptr_t)rows * (uintptr_t)dim * 4u, lb = (uintptr_t)rows * 4u;
+    const uintptr_t a[4] = {(uintptr_t)o, (uintptr_t)lse, (uintptr_t)o_part, (uintptr_t)lse_part};
+    const uintptr_t n[4] = {ob, lb, ob, lb};
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (a[i] < a[j] + n[j] && a[j] < a[i] + n[i]) return SHATTN_EINVAL;
+  }
+
+  const int64_t es = elem_size(desc->in_dtype);
+  const int64_t clen = kv_len_total / num_chunks;
+  // Position of the last query: a causal chunk starting after it is seen by
+  // no query, so it is neither fetched nor computed.
+  const int64_t q_last = desc->q_pos0 + desc->seq_q - 1;
+  auto chunk_ptr = [&](const void* base, const int64_t* stride, int64_t c) {
+    return (const char*)base + c * clen * stride[2] * es;
+  };
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t r) {
+    if (e == hipSuccess) e = r;
+    return e == hipSuccess;
+  };
+  // The copies overwrite k and v: they wait for the work already on the
+  // compute stream, which may still read them.
+  hipEvent_t ev;
+  if (!ok(hipEventCreateWithFlags(&ev, hipEventDisableTiming))) return SHATTN_EHIP;
+  ok(hipEventRecord(ev, compute_stream));
+  ok(hipStreamWaitEvent(copy_stream, ev, 0));
+  ok(hipEventDestroy(ev));
+  auto copy_chunk = [&](const void* src, void* dst, const int64_t* st, int64_t c) {
+    const int64_t row_b = dim * es, pitch = st[2] * es;
+    const char* s0 = chunk_ptr(src, st, c);
+    char* d0 = (char*)chunk_ptr(dst, st, c);
+    if (st[2] == dim) {
+      const int64_t block = clen * row_b;
+      const int32_t nb = desc->batch, nh = desc->heads_kv;
+      if ((int64_t)nb * nh == 1) {
+        ok(hipMemcpyAsync(d0, s0, block, hipMemcpyDefault, copy_stream));
+      } else if ((nb == 1 || st[0] == nh * st[1]) && st[1] * es >= block) {
+        ok(hipMemcpy2DAsync(d0, st[1] * es, s0, st[1] * es, block, (size_t)nb * nh,
+                            hipMemcpyDefault, copy_stream));
+      } else {
+        for (int32_t b = 0; b < nb && e == hipSuccess; ++b)
+          for (int32_t hk = 0; hk < nh && e == hipSuccess; ++hk) {
+            const int64_t off = (b * st[0] + hk * st[1]) * es;
+            ok(hipMemcpyAsync(d0 + off, s0 + off, block, hipMemcpyDefault, copy_stream));
+          }
+      }
+      return;
+    }
+    for (int32_t b = 0; b < desc->batch && e == hipSuccess; ++b)
+      for (int32_t hk = 0; hk < desc->heads_kv && e == hipSuccess; ++hk) {
+        const int64_t off = (b * st[0] + hk * st[1]) * es;
+        ok(hipMemcpy2DAsync(d0 + off, pitch, s0 + off, pitch, row_b, clen, hipMemcpyDefault,
+                            copy_stream));
+      }
+  };
+  bool first = true;
+  for (int32_t j = 0; j < num_chunks && e == hipSuccess && !kv_empty; ++j) {
+    const int64_t c = (j + rank) % num_chunks;
+    if (desc->causal && c * clen > q_last) continue;
+    // Chunk c's rows of every (batch, KV head) slice, at the same offsets in
+    // source and destination, in as few copies as the layout allows: with
+    // rows back to back (sequence stride == head_dim) one slice's chunk is a
+    // single block, and evenly spaced slices make one 2-D copy of blocks.
+    // Chunk `rank` (j = 0) is the rank's own: it is already in k, v.
+    if (j > 0) {
+      copy_chunk(k_src, k, desc->k_stride, c);
+      copy_chunk(v_src, v, desc->v_stride, c);
+      if (!ok(hipEventCreateWithFlags(&ev, hipEventDisableTiming))) break;
+      ok(hipEventRecord(ev, copy_stream));
+      ok(hipStreamWaitEvent(compute_stream, ev, 0));
+      ok(hipEventDestroy(ev));
+      if (e != hipSuccess) break;
+    }
+    // Partial of Q against chunk c, merged into (o, lse) in visit order.
+    st = attn_chunk_fwd(desc, q, chunk_ptr(k, desc->k_stride, c), chunk_ptr(v, desc->v_stride, c),
+                        clen, c * clen, first ? o : o_part, first ? lse : lse_part,
+                        compute_stream);
+    if (st == SHATTN_OK && !first)
+      st = lse_merge(rows, (int32_t)dim, o, lse, o_part, lse_part, compute_stream);
+    if (st != SHATTN_OK) return st;
+    first = false;
+  }
+  if (e != hipSuccess) return SHATTN_EHIP;
+  // No chunk visible to any query: O = 0, LSE = -inf.
+  if (first) return attn_chunk_fwd(desc, q, k, v, 0, 0, o, lse, compute_stream);
+  return SHATTN_OK;
 }
 
 const char* attn_status_string(int status) {

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
     assert set(names) == {"attn_chunk_fwd", "lse_merge", "attn_shifted_fwd",
-                          "attn_status_string"}
+                          "attn_shifted_fwd_overlapped", "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -139,6 +139,40 @@ def test_chunk_rejects_bad_arguments():
     assert _chunk(lib, d, kv_len=(1 << 31) - 63) == 2
     # o_part is fp32: a row stride of 6 floats (24 bytes) is not 16-byte aligned.
     assert _chunk(lib, _desc(o_stride=S3(6, 6, 6)), kv_len=256) == 1
+
+
+S1, S2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)  # stream handles, never used
+
+
+def _overlapped(lib, d, q=FAKE, ksrc=FAKE, vsrc=FAKE, k=FAKE, v=FAKE, total=1024, nch=4, rank=1,
+                o=0x1000000, lse=0x2000000, op=0x3000000, lp=0x4000000, cs=S1, ps=S2):
+    return lib.attn_shifted_fwd_overlapped(ctypes.byref(d) if d is not None else None, q, ksrc,
+                                           vsrc, k, v, total, nch, rank, o, lse, op, lp, cs, ps)
+
+
+def test_overlapped_rejects_bad_arguments():
+    lib = _lib()
+    d = _desc()  # O strides are the contiguous [1, 4, 256, 128] ones
+    assert _overlapped(lib, None) == 1
+    assert _overlapped(lib, d, rank=4) == 1
+    assert _overlapped(lib, d, total=1000, nch=3) == 1
+    assert _overlapped(lib, d, cs=None, ps=None) == 1          # one stream for both
+    assert _overlapped(lib, d, cs=S1, ps=S1) == 1
+    assert _overlapped(lib, d, ksrc=0) == 1
+    assert _overlapped(lib, d, vsrc=0) == 1
+    assert _overlapped(lib, d, k=0) == 1
+    assert _overlapped(lib, d, op=0) == 1
+    assert _overlapped(lib, d, op=0x3000000 + 4) == 1           # misaligned partial
+    assert _overlapped(lib, d, op=0x1000000 + 4096) == 1        # partial inside O
+    assert _overlapped(lib, d, lp=0x3000000 + 64) == 1          # LSE partial inside O partial
+    assert _overlapped(lib, d, lse=0x4000000 + 4) == 1          # the two LSE buffers overlap
+    assert _overlapped(lib, _desc(o_stride=S3(2 * 4 * 256 * 128, 256 * 128, 128))) == 1
+    assert _overlapped(lib, _desc(head_dim=64)) == 2
+    assert _overlapped(lib, _desc(k_stride=S3(4 * 256 * 128, 256 * 128, 64))) == 1  # rows overlap
+    assert _overlapped(lib, d, total=(1 << 31) - 56, nch=8) == 2
+    # No query rows: nothing to do, nothing enqueued.
+    empty = _desc(seq_q=0, o_stride=S3(0, 0, 128))
+    assert _overlapped(lib, empty, q=0, o=0, lse=0, op=0, lp=0) == 0
 
 
 def test_merge_rejects_bad_arguments():

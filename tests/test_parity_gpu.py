@@ -246,6 +246,69 @@ def test_kv_sharded_partials_tree_merge(din):
     assert float((lse_lin - lse).abs().max()) <= 1e-5
 
 
+def _pinned_like(t, layout_bshd=False):
+    """A pinned host copy of device tensor t with the same strides."""
+    if layout_bshd:
+        b, h, s_, d = t.shape
+        host = torch.empty((b, s_, h, d), dtype=t.dtype, pin_memory=True).permute(0, 2, 1, 3)
+    else:
+        host = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    host.copy_(t.cpu())
+    assert host.stride() == t.stride()
+    return host
+
+
+@pytest.mark.parametrize("case", [
+    # (B, Hq, Hkv, Sq, Skv, J, rank, causal, q_pos0, dtype, source, K/V layout [B,S,H,D])
+    (1, 4, 2, 300, 1024, 8, 3, True, 384, torch.bfloat16, "host", False),
+    (2, 4, 4, 130, 768, 3, 2, False, 0, torch.bfloat16, "host", True),
+    (1, 2, 1, 200, 600, 5, 4, True, 400, torch.float32, "host", False),
+    (1, 4, 2, 256, 512, 4, 1, True, 128, torch.bfloat16, "device", False),
+], ids=lambda c: "x".join(str(v) for v in c[:9]) + "-" + c[10] + ("-bshd" if c[11] else ""))
+def test_overlapped_chunk_walk(case):
+    """Chunks copied in visit order on a second stream while earlier chunks
+    compute: equal to the resident chunk-by-chunk walk, and to the oracle.
+    The device K/V start as NaN except for the rank's own chunk, so a chunk
+    read before its copy landed, or a causally invisible chunk that was
+    computed, would show up."""
+    b, hq, hkv, sq, skv, nch, rank, causal, q_pos0, din, source, bshd = case
+    _say(f"overlapped chunk walk {case}")
+    q, k, v = gen_qkv(batch=b, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=din, device=DEV, seed=91)
+    if bshd:
+        k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    if source == "host":
+        k_src, v_src = _pinned_like(k, bshd), _pinned_like(v, bshd)
+    else:
+        k_src, v_src = k.clone(), v.clone()
+    k_dev = torch.full_like(k, float("nan"))
+    v_dev = torch.full_like(v, float("nan"))
+    clen = skv // nch
+    own = slice(rank * clen, (rank + 1) * clen)
+    k_dev[:, :, own] = k[:, :, own]
+    v_dev[:, :, own] = v[:, :, own]
+    torch.cuda.synchronize()
+    o, lse = binding.attn_shifted_fwd_overlapped(q, k_src, v_src, k_dev, v_dev, num_chunks=nch,
+                                                 rank=rank, causal=causal, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    q_last = q_pos0 + sq - 1
+    for c in range(nch):
+        seen = not causal or c * clen <= q_last
+        part = k_dev[:, :, c * clen:(c + 1) * clen]
+        if seen:
+            assert torch.equal(part, k[:, :, c * clen:(c + 1) * clen]), f"chunk {c} not copied"
+        else:
+            assert bool(torch.isnan(part).all()), f"invisible chunk {c} was copied"
+    o_res, lse_res = _composed(q, k, v, nch, rank, causal, q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_res) and torch.equal(lse, lse_res)
+    o_ref, lse_ref = oracle.shifted_attention(q.cpu(), k.cpu(), v.cpu(), num_chunks=nch,
+                                              rank=rank, causal=causal, q_pos0=q_pos0)
+    assert _max_err(o, o_ref) <= TOL_O[din]
+    _check_lse(lse, lse_ref)
+
+
 @pytest.mark.parametrize("din", [torch.bfloat16, torch.float32])
 def test_chunk_fwd_ragged_and_masked(din):
     _say(f"chunk fwd ragged/masked {din}")
