@@ -414,22 +414,6 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, const f32x4& v) {
   *(bf16x4*)dst = x;
 }
 
-// Keys of a tile that a query cannot see become -inf: keys at or past t_end,
-// and (causal) keys after the query's global position.  rel0 = (global
-// position of the block's first query) - t0, a wave-uniform value; the
-// lane's query is rel0 + lq positions past the tile start.
-__device__ __forceinline__ void mask_block(f32x16& s0, f32x16& s1, bool causal, int rel0,
-                                           int last, int lq, int hh) {
-  const int rel = causal ? max(min(rel0, kN), -kN) : kN;
-  const int lim = min(rel + (causal ? lq : 0), last) - 4 * hh;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int koff = 8 * (r >> 2) + (r & 3);
-    s0[r] = koff <= lim ? s0[r] : -INFINITY;
-    s1[r] = koff + 32 <= lim ? s1[r] : -INFINITY;
-  }
-}
-
 // Makes the compiler wait for outstanding loads into v before going on.
 template <typename T>
 __device__ __forceinline__ void settle(const T& v) {
@@ -964,9 +948,80 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     tile_barrier();
     if (xt + 2 < n_rest) copy_rest(xt + 2);
     const __bf16* ktile = &lds_k[rslot][0];
-    {
-      // K operands two steps ahead.
-      bf16x8 ka[3];
+    const int last = t_end - 1 - t0;
+    const bool dead = (p.causal && t0 > wave_q_max) || wave_q0 >= p.seq_q;
+    // P V; a wave none of whose queries sees the tile reads the zero tile.
+    const uint32_t vrel =
+        lds_address(dead ? lds_vzero : &lds_v[rslot][0]) - lds_address(&lds_v[0][0]);
+    // Four phases of 16 matrix ops: S of query block 0, S of block 1, P V of
+    // block 0, P V of block 1.  Block 0's softmax runs under phase 2, block
+    // 1's under phase 3; each block's last eight probability pairs spill
+    // into the next phase, ahead of the ops that read them.  Scores are read
+    // no sooner than eight ops after the op that wrote them.
+    float mxq[2] = {-INFINITY, -INFINITY};
+    float rsum[2] = {0.f, 0.f};
+    bool move[2] = {false, false};
+    float alpha[2] = {1.f, 1.f};
+    // Keys a query cannot see become -inf: keys at or past t_end, and
+    // (causal) keys after the query's global position.  The block's first
+    // query sits rel_block(..) - t0 positions past the tile start (clamped
+    // to [-kN, kN]), the lane's query lq further.
+    auto mask_rows = [&](int qb, int kb, int r0) {
+      // Rows r0..r0+3 of key block kb: mask, then fold into the row max.
+      const int rel = p.causal ? max(min(rel_block(wave_q0 + 32 * qb) - t0, kN), -kN) : kN;
+      const int lim = min(rel + (p.causal ? lq : 0), last) - 4 * hh - 32 * kb;
+#pragma unroll
+      for (int r = r0; r < r0 + 4; ++r) {
+        const int koff = 8 * (r >> 2) + (r & 3);
+        s[kb][qb][r] = koff <= lim ? s[kb][qb][r] : -INFINITY;
+      }
+      mxq[qb] = vmax(vmax(mxq[qb], s[kb][qb][r0]), s[kb][qb][r0 + 1]);
+      mxq[qb] = vmax(vmax(mxq[qb], s[kb][qb][r0 + 2]), s[kb][qb][r0 + 3]);
+    };
+    auto ref_update = [&](int qb) {
+      const float m_tile = lane_swap32_max(mxq[qb]) * c;
+      // The reference moves under the same rule as in the main walk (a
+      // row's first visible keys always move it: -inf + slack = -inf).
+      move[qb] = m_tile > m_ref[qb] + kRescaleSlack;
+      const float m_new = move[qb] ? m_tile : m_ref[qb];
+      alpha[qb] = move[qb] ? exp2_fast(m_ref[qb] - m_new) : 1.f;
+      m_ref[qb] = m_new;
+      m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
+      l_run[qb] *= alpha[qb];
+    };
+    auto exp_job = [&](int qb, int i) {  // probability pair i (0..15) of block qb
+      exp_pair(s[i >> 3][qb], 2 * (i & 7), c, m_use[qb], pb[qb][i >> 2], (2 * i) & 7, rsum[qb]);
+    };
+    // Softmax slice of block qb under step st of a phase hosting it.
+    auto softmax_slice = [&](int qb, int st) {
+      if (st < 4) mask_rows(qb, 0, 4 * st);
+      else if (st >= 8 && st < 12) mask_rows(qb, 1, 4 * (st - 8));
+      if (st == 12) ref_update(qb);
+      if (st >= 12) {
+        exp_job(qb, 2 * (st - 12));
+        exp_job(qb, 2 * (st - 12) + 1);
+      }
+    };
+    // The rest of block qb's pairs (8..15) under steps 0..3 of the next phase.
+    auto exp_tail = [&](int qb, int st) {
+      if (st < 4) {
+        exp_job(qb, 8 + 2 * st);
+        exp_job(qb, 9 + 2 * st);
+      }
+      if (st == 3) l_run[qb] += rsum[qb];
+    };
+    auto rescale_o = [&](int qb) {
+      if (__builtin_amdgcn_ballot_w64(move[qb]) != 0) {
+        matrix_settle();
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          __builtin_amdgcn_sched_barrier(0);
+          agpr_set(o[qb][db], agpr_get(o[qb][db]) * alpha[qb]);
+        }
+      }
+    };
+    auto qk_phase = [&](int qb, auto&& extra) {
+      bf16x8 ka[3];  // K operands two steps ahead
       ka[0] = read_k(ktile, koff, 0, 0);
       ka[1] = read_k(ktile, koff, 0, 1);
 #pragma unroll
@@ -974,63 +1029,34 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         const int kb = t >> 3, kk = t & 7;
         if (t + 2 < 16) ka[(t + 2) % 3] = read_k(ktile, koff, (t + 2) >> 3, (t + 2) & 7);
-        if (kk == 0) {
-          qk_mfma0(s[kb][0], ka[t % 3], qv[0][kk]);
-          qk_mfma0(s[kb][1], ka[t % 3], qv[1][kk]);
-        } else {
-          qk_mfma(s[kb][0], ka[t % 3], qv[0][kk]);
-          qk_mfma(s[kb][1], ka[t % 3], qv[1][kk]);
-        }
+        if (kk == 0) qk_mfma0(s[kb][qb], ka[t % 3], qv[qb][kk]);
+        else qk_mfma(s[kb][qb], ka[t % 3], qv[qb][kk]);
+        extra(t);
       }
-    }
-    matrix_settle();
-    const int last = t_end - 1 - t0;
-    const bool dead = (p.causal && t0 > wave_q_max) || wave_q0 >= p.seq_q;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      mask_block(s[0][qb], s[1][qb], p.causal != 0, rel_block(wave_q0 + 32 * qb) - t0, last, lq, hh);
-      float mxq = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mxq = vmax(vmax(mxq, s[0][qb][r]), s[1][qb][r]);
-      const float m_tile = lane_swap32_max(mxq) * c;
-      // The reference moves under the same rule as in the main walk (a
-      // row's first visible keys always move it: -inf + slack = -inf).
-      const bool move = m_tile > m_ref[qb] + kRescaleSlack;
-      const float m_new = move ? m_tile : m_ref[qb];
-      const float alpha = move ? exp2_fast(m_ref[qb] - m_new) : 1.f;
-      m_ref[qb] = m_new;
-      m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
-      l_run[qb] *= alpha;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          __builtin_amdgcn_sched_barrier(0);
-          agpr_set(o[qb][db], agpr_get(o[qb][db]) * alpha);
-        }
-      }
-      float rsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        exp_pair(s[i >> 3][qb], 2 * (i & 7), c, m_use[qb], pb[qb][i >> 2], (2 * i) & 7, rsum);
-      l_run[qb] += rsum;
-    }
-    // P V; a wave none of whose queries sees the tile reads the zero tile.
-    const uint32_t vrel =
-        lds_address(dead ? lds_vzero : &lds_v[rslot][0]) - lds_address(&lds_v[0][0]);
-    matrix_settle();
-    {
-      // V operands two steps ahead.
-      bf16x8 va[3];
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pv_phase = [&](int qb, auto&& extra) {
+      bf16x8 va[3];  // V operands two steps ahead
       va[0] = read_v(vrel, voff, 0, 0);
       va[1] = read_v(vrel, voff, 0, 1);
 #pragma unroll
       for (int st = 0; st < 16; ++st) {
         __builtin_amdgcn_sched_barrier(0);
         if (st + 2 < 16) va[(st + 2) % 3] = read_v(vrel, voff, (st + 2) >> 2, (st + 2) & 3);
-        pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
-        pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+        pv_mfma(o[qb][st & 3], va[st % 3], pb[qb][st >> 2]);
+        extra(st);
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    qk_phase(0, [&](int) {});
+    qk_phase(1, [&](int t) { softmax_slice(0, t); });
+    rescale_o(0);
+    pv_phase(0, [&](int st) {
+      exp_tail(0, st);
+      softmax_slice(1, st);
+    });
+    rescale_o(1);
+    pv_phase(1, [&](int st) { exp_tail(1, st); });
     matrix_settle();
   }
 
