@@ -429,6 +429,9 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // the tile (P known to be zero), so that non-finite values in a V tile no
   // query of the wave can see never reach it through 0 * NaN.
   __shared__ __attribute__((aligned(16))) __bf16 lds_vzero[kTile];
+  // Wave 3's staging area for its Q rows (waves 0-2 stage theirs in K ring
+  // slot 3, V ring slot 2 and the zero tile, all free at an item's start).
+  __shared__ __attribute__((aligned(16))) __bf16 lds_qx[kTile];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in [0, 4)
@@ -496,8 +499,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const Walk walk = make_walk(a0, a_main, 0, b_main);
   const Walk rest_walk = make_walk(a_main, a_lim, b_main, b_lim);
   const int n_tiles = walk.n;
-  const int wave_q_min = rel(wave_q0);
-  // Last query of the wave (below wave_q_min if the wave has no rows).
+  // Last query of the wave (below its first, rel(wave_q0), if the wave has
+  // no rows).
   const int wave_q_max = rel(min(wave_q0 + 63, p.seq_q - 1));
 
   const __bf16* qbase = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
@@ -541,24 +544,42 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     for (int n = 0; n < 4; ++n) copy_v(tc, cl, n, wave, lane);
   };
 
-  // Q^T operands of both query blocks, resident in AGPRs for the whole kernel.
-  bf16x8 qv[2][8];
+  // Q rows of the wave go through LDS: 16 copies of four whole rows each
+  // (laid out and swizzled like a K tile), read back below as the Q^T
+  // operands.  Rows past the end of the shard copy its last row (their
+  // results are never stored).
+  const __bf16* const q_stage = wave == 0 ? &lds_k[kRing - 1][0]
+                              : wave == 1 ? &lds_v[2][0]
+                              : wave == 2 ? lds_vzero
+                                          : lds_qx;
+  {
+    const int64_t q_hi = p.seq_q - 1;
+    const uint32_t q_stride_b = (uint32_t)p.q_ss * 2u;
+    const uint32_t qdst = lds_address(q_stage);
+    if (wave_q0 + 63 <= q_hi) {
+      // All 64 rows exist: instruction n copies rows 4n..4n+3; the row step
+      // goes into the (scalar) base, the lane offset repeats every 4 n.
+      uint32_t off[4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t my_q = wave_q0 + 32 * qb + lq;
-    const bool row_ok = my_q < p.seq_q;
-    const int64_t row = row_ok ? my_q : 0;
+      for (int m = 0; m < 4; ++m)
+        off[m] = (uint32_t)(lane >> 4) * q_stride_b + k_chunk(4 * m + (lane >> 4), lane);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const u32x4 x = *(const u32x4*)(qbase + row * p.q_ss + kk * 16 + hh * 8);
-      u32x4 y;
-      y[0] = row_ok ? x[0] : 0u;
-      y[1] = row_ok ? x[1] : 0u;
-      y[2] = row_ok ? x[2] : 0u;
-      y[3] = row_ok ? x[3] : 0u;
-      agpr_set(qv[qb][kk], __builtin_bit_cast(bf16x8, y));
+      for (int n = 0; n < 16; ++n)
+        copy_one(qdst + 1024u * n, uniform_ptr(qbase + (wave_q0 + 4 * n) * p.q_ss), off[n & 3]);
+    } else {
+      // The shard's last rows: rows past its end copy row q_hi.
+      const int64_t q_w = min(wave_q0, q_hi);
+      const __bf16* qsrc = uniform_ptr(qbase + q_w * p.q_ss);
+      const int r_lim = __builtin_amdgcn_readfirstlane((int)min(q_hi - q_w, (int64_t)63));
+      for (int n = 0; n < 16; ++n) {
+        const int row = 4 * n + (lane >> 4);
+        const uint32_t r = (uint32_t)min(row, r_lim);
+        copy_one(qdst + 1024u * n, qsrc, r * q_stride_b + k_chunk(row, lane));
+      }
     }
   }
+  // Q^T operands of both query blocks, resident in AGPRs for the whole kernel.
+  bf16x8 qv[2][8];
 
   // Per-lane LDS byte offsets of the matrix-core operands (see read_k, read_v).
   int koff[8];
@@ -577,12 +598,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const float c = p.scale_log2;
   {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < kTile / 8; i += kThreads) {
-      *(u32x4*)(lds_vzero + 8 * i) = zero;
-      // The main walk's first tile multiplies P = 0 into V ring slot 3 (the
-      // slot of "tile -1"), which no copy writes before tile 1.
+    // The main walk's first tile multiplies P = 0 into V ring slot 3 (the
+    // slot of "tile -1"), which no copy writes before tile 1.  (The zero
+    // tile is refilled below, once wave 2 has read its Q rows from it.)
+    for (int i = tid; i < kTile / 8; i += kThreads)
       *(u32x4*)(&lds_v[kRing - 1][0] + 8 * i) = zero;
-    }
   }
   f32x16 o[2][4];
   float m_ref[2], m_use[2];  // reference max; m_use = m_ref, or 0 while it is -inf
@@ -634,6 +654,17 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   }
   if (n_tiles > 2) copy_tile_k(k_copy(walk, 2, 2));
   wait_copies(0);
+  // This wave's Q rows are in: take the operands.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) agpr_set(qv[qb][kk], read_k(q_stage, koff, qb, kk));
+  if (wave == 2) {
+    // Wave 2 staged its Q in the zero tile: zero it again.
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kTile / 8 / 64; ++i) *(u32x4*)(lds_vzero + 8 * (64 * i + lane)) = zero;
+  }
   __syncthreads();
 
   int slot = 0;

@@ -91,3 +91,53 @@ def test_built_kernels_keep_matrix_core_wait_states(source, tmp_path):
     assert "v_mfma" in text or source == "lse_merge.hip"
     hazards = check(text)
     assert not hazards, "\n".join(str(h) for h in hazards[:20])
+
+
+def _m0_writers_outside_asm(text):
+    """Instructions outside inline-assembly blocks that write M0, or copy
+    instructions (which read M0) that the compiler emitted itself."""
+    bad, in_asm = [], False
+    for line in text.splitlines():
+        s = line.split(";")[0].strip() if not line.strip().startswith(";;#ASM") else line.strip()
+        if s == ";;#ASMSTART":
+            in_asm = True
+            continue
+        if s == ";;#ASMEND":
+            in_asm = False
+            continue
+        if not s or in_asm:
+            continue
+        op = s.split()[0]
+        args = s[len(op):].replace(" ", "").split(",")
+        if (op.startswith("s_") and args and args[0] == "m0") or "_lds_" in op:
+            bad.append(s)
+    return bad
+
+
+def test_m0_checker_flags_a_compiler_write():
+    text = "\n".join(["kern:", "\ts_mov_b32 m0, -1", "\t;;#ASMSTART",
+                      "\tglobal_load_lds_dwordx4 v0, s[4:5]", "\t;;#ASMEND", "\ts_endpgm"])
+    assert _m0_writers_outside_asm(text) == ["s_mov_b32 m0, -1"]
+    ok = "\n".join(["kern:", "\t;;#ASMSTART", "\ts_mov_b32 m0, s3", "\ts_nop 0",
+                    "\tglobal_load_lds_dwordx4 v0, s[4:5]", "\t;;#ASMEND", "\ts_endpgm"])
+    assert _m0_writers_outside_asm(ok) == []
+
+
+def test_built_bf16_kernel_leaves_m0_to_its_copies(tmp_path):
+    """The global->LDS copies take their LDS address from M0, written by the
+    kernel's own assembly one or more instructions earlier (in the hot loop,
+    a schedule step earlier).  The compiler treats M0 as reserved and may not
+    honour an asm clobber of it, so the build must show that the compiler
+    itself never writes M0 and emits no M0-reading copy of its own."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    flags = [f for f in libbuild.HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    out = tmp_path / "bf16.s"
+    cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(libbuild.ROOT, "include"),
+           "-o", str(out), os.path.join(libbuild.CSRC, "attn_fwd_bf16.hip")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    assert "global_load_lds_dwordx4" in text
+    assert _m0_writers_outside_asm(text) == []
