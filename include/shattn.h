@@ -14,10 +14,12 @@
  * so the definitions below are the textbook ones.
  *
  * Common rules for every entry point:
- *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *  - All tensor pointers are DEVICE pointers owned by the caller (the
+ *    overlapped walk's sources may also be pinned host memory).  The
  *    library never allocates, frees or retains user memory.
- *  - Calls only enqueue work on `stream` (0 = the null stream) and never
- *    synchronize; outputs are valid once the stream reaches that point.
+ *  - Calls only enqueue work on their stream(s) (0 = the null stream) and
+ *    never synchronize; outputs are valid once the stream reaches that
+ *    point.
  *  - Every argument is validated on the host before anything is launched; on
  *    failure the call returns a non-zero status and launches nothing.  No
  *    exceptions cross this boundary and nothing aborts.
