@@ -514,6 +514,34 @@ def test_shifted_random_sweep(case):
     _check_lse(lse, lse_ref)
 
 
+def _sweep_cases_multi_tile(n, seed):
+    """Like _sweep_cases, at sizes that span several 256-row query tiles (so
+    waves wholly past the shard's end, ragged last tiles and several work
+    items per workgroup all occur) and keys in up to 16 chunks."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        hq = hkv * int(rng.integers(1, 5))
+        nch = int(rng.integers(1, 17))
+        skv = nch * int(rng.integers(16, 257))
+        sq = int(rng.integers(300, 1500))
+        rank = int(rng.integers(0, nch))
+        causal = bool(rng.integers(0, 2))
+        q_pos0 = int(rng.integers(0, skv)) if causal else 0
+        din = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+        dout = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        cases.append((1 + int(rng.integers(0, 2)), hq, hkv, sq, skv, nch, rank, causal, q_pos0,
+                      din, dout))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases_multi_tile(12, seed=2027),
+                         ids=lambda c: "x".join(str(v) for v in c[:9]))
+def test_shifted_random_sweep_multi_tile(case):
+    test_shifted_random_sweep(case)
+
+
 @pytest.mark.parametrize("main_tiles", [1, 2, 3, 4, 5])
 def test_short_main_walks(main_tiles):
     """A workgroup whose unmasked walk holds 1..5 tiles: the tile copies that
