@@ -253,6 +253,44 @@ def overlap_report(w, q, k, v, steps: int, warmup: int):
     return 0
 
 
+def merge_report(w, steps: int, warmup: int):
+    """One JSON line on lse_merge alone, over the workload's rows (B*Hq*Sq
+    rows of head_dim fp32): HBM-bound, priced against 8 TB/s with its
+    algorithmic bytes (read O_a, O_b and two LSEs, write O and one LSE)."""
+    import torch
+
+    from long_context_attention_attn_amd import binding
+
+    dev = torch.device("cuda", 0)
+    rows = w.batch * w.heads_q * w.seq_q
+    gen = torch.Generator(device=dev).manual_seed(5)
+    o_a = torch.randn((rows, w.head_dim), generator=gen, device=dev)
+    o_b = torch.randn((rows, w.head_dim), generator=gen, device=dev)
+    l_a = torch.randn(rows, generator=gen, device=dev)
+    l_b = torch.randn(rows, generator=gen, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        binding.lse_merge(o_a, l_a, o_b, l_b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        binding.lse_merge(o_a, l_a, o_b, l_b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(steps, 1)
+    nbytes = rows * (3 * w.head_dim * 4 + 3 * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "lse_merge HBM throughput", "workload": w.name, "rows": rows,
+        "head_dim": w.head_dim, "steps": steps, "warmup": warmup, "ms_per_merge": round(ms, 5),
+        "bytes_per_merge": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+    }), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +304,8 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0)
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
     ap.add_argument("--flush-mib", type=int, default=0)
+    ap.add_argument("--lse-merge", action="store_true",
+                    help="time lse_merge alone over the workload's rows")
     ap.add_argument("--overlap-from-host", action="store_true",
                     help="time the overlapped chunk walk with K/V in pinned host memory")
     args = ap.parse_args()
@@ -285,6 +325,8 @@ def main():
     from long_context_attention_attn_amd.workloads import BY_NAME, make_inputs
 
     w = BY_NAME[args.workload]
+    if args.lse_merge:
+        return merge_report(w, args.steps, args.warmup)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log(f"bench: workload {w.name}: generating inputs")
