@@ -70,46 +70,81 @@ def read_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """The fp64 oracle on the host, over whole (batch, head) slices of the
-    same workload until ``budget_s`` seconds have passed."""
-    import numpy as np
-    import oracle
-
+def _blas_info():
+    """Vendor, version and thread count of the BLAS numpy uses."""
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                return {"vendor": p.get("internal_api"), "version": p.get("version"),
+                        "threads": p.get("num_threads")}
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+    return {"vendor": None, "version": None, "threads": None}
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The fp64 oracle on the host, over whole (batch, head) slices of the
+    same workload until ``budget_s`` seconds of oracle time have passed.
+
+    The BLAS pool is set to every core this process may run on.  Moving a
+    slice to the host and upcasting it to fp64 is timed apart from the
+    oracle call, which then receives fp64 arrays."""
+    import numpy as np
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        limiter = None
     group = w.heads_q // w.heads_kv
     done_flops = 0
     slices = 0
-    t_start = time.perf_counter()
     elapsed = 0.0
+    prep = 0.0
+    nk = w.visible_kv_rows()
+    rows = np.arange(w.seq_q)
+    kv_cache = {}
     for b in range(w.batch):
         for h in range(w.heads_q):
             hk = h // group
-            rows = np.arange(w.seq_q)
-            qs, ks, vs = (q[b:b + 1, h:h + 1].cpu(), k[b:b + 1, hk:hk + 1].cpu(),
-                          v[b:b + 1, hk:hk + 1].cpu())
             t0 = time.perf_counter()
+            if (b, hk) not in kv_cache:
+                kv_cache.clear()
+                kv_cache[(b, hk)] = (k[b, hk, :nk].cpu().double().numpy()[None, None],
+                                     v[b, hk, :nk].cpu().double().numpy()[None, None])
+            ks, vs = kv_cache[(b, hk)]
+            qs = q[b, h].cpu().double().numpy()[None, None]
+            t1 = time.perf_counter()
             oracle.attention_rows(qs, ks, vs, 0, 0, rows, causal=w.causal, q_pos0=w.q_pos0)
-            elapsed += time.perf_counter() - t0
+            t2 = time.perf_counter()
+            prep += t1 - t0
+            elapsed += t2 - t1
             done_flops += 4 * w.head_dim * w.visible_pairs_per_head()
             slices += 1
-            if time.perf_counter() - t_start >= budget_s:
+            if elapsed >= budget_s:
                 break
         else:
             continue
         break
+    blas = _blas_info()
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {
         "value": done_flops / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(cores),
         "kind": "oracle",
         "sample": f"{slices} of {w.batch * w.heads_q} (batch, query-head) slices, every row, "
-                  f"fp64 numpy; {elapsed:.1f} s",
+                  f"fp64 numpy; oracle {elapsed:.1f} s, host copy + fp64 upcast {prep:.1f} s "
+                  "(not in the rate)",
+        "blas": blas,
+        "oracle_s": round(elapsed, 2),
+        "upcast_s": round(prep, 2),
     }
 
 
@@ -348,8 +383,6 @@ def main():
     # The kernel runs on torch's current stream; events on that same stream
     # bracket exactly the K launches.
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -363,14 +396,20 @@ def main():
             step()
             ends[i].record(stream)
         torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / max(args.steps, 1)
+        per_launch = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+        ms = sum(per_launch) / max(args.steps, 1)
     else:
-        ev0.record(stream)
-        for _ in range(args.steps):
+        # One event before every launch and one after the last: the first and
+        # last bracket the K launches (the mean), neighbours give each
+        # launch's own time (median and minimum).
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        for i in range(args.steps):
+            evs[i].record(stream)
             step()
-        ev1.record(stream)
+        evs[-1].record(stream)
         torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
+        ms = evs[0].elapsed_time(evs[-1]) / max(args.steps, 1)
+        per_launch = sorted(a.elapsed_time(b) for a, b in zip(evs[:-1], evs[1:]))
     t_wall = time.perf_counter() - t_wall
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -408,6 +447,12 @@ def main():
             "causal": w.causal, "algorithmic_gflop": round(flops / 1e9, 3),
             "parallelism": "one rank's shard on 1 GPU",
             "cache_flush_mib": args.flush_mib,
+        },
+        "launch_ms": {
+            "mean": round(ms, 5),
+            "median": round(per_launch[len(per_launch) // 2], 5) if per_launch else None,
+            "min": round(per_launch[0], 5) if per_launch else None,
+            "max": round(per_launch[-1], 5) if per_launch else None,
         },
         "roofline": {
             "bound": "mfma",

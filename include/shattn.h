@@ -24,6 +24,13 @@
  *    failure the call returns a non-zero status and launches nothing.  No
  *    exceptions cross this boundary and nothing aborts.
  *  - NaN/Inf in inputs propagate to the outputs; they are never masked.
+ *  - Range (bf16 inputs): the softmax keeps a per-row reference that moves
+ *    only when a score exceeds it by more than 64 in log2 units, so an
+ *    unnormalised output element can reach n * 2^64 * max|v| for a row with
+ *    n visible keys.  Outputs are finite whenever max|v| * n < 2^64 (fp32
+ *    accumulators overflow at 2^128); beyond that an output may become inf
+ *    where the exact result is finite.  The fp32 path keeps a true running
+ *    max and has no such limit.
  *  - Calls are stateless and thread-safe.
  */
 #ifndef SHATTN_H

@@ -119,9 +119,32 @@ def _strides(t: torch.Tensor):
     return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
-def make_desc(q, k, v, o, *, causal: bool, q_pos0: int, scale, out_dtype) -> ShattnDesc:
+def _check_shapes(q, k, v, o, lse):
+    """The C ABI sees pointers and strides only: every size it derives from
+    ``q`` must hold for the other tensors, or a kernel would run past one of
+    them.  K/V: [B, Hkv, Skv, D] with Hq % Hkv == 0; O: q's shape; LSE:
+    [B, Hq, Sq]."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", o)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, S, D], got {tuple(t.shape)}")
+    b, hq, sq, dim = q.shape
+    if k.shape != v.shape:
+        raise ValueError(f"K {tuple(k.shape)} and V {tuple(v.shape)} differ in shape")
+    if k.shape[0] != b or k.shape[3] != dim:
+        raise ValueError(f"K/V {tuple(k.shape)} do not match Q {tuple(q.shape)} in batch "
+                         "or head_dim")
+    if k.shape[1] < 1 or hq % k.shape[1] != 0:
+        raise ValueError(f"query heads {hq} are not a multiple of KV heads {k.shape[1]}")
+    if tuple(o.shape) != (b, hq, sq, dim):
+        raise ValueError(f"output {tuple(o.shape)} does not match Q {tuple(q.shape)}")
+    if lse is not None and tuple(lse.shape) != (b, hq, sq):
+        raise ValueError(f"LSE {tuple(lse.shape)} is not [B, Hq, Sq] = {(b, hq, sq)}")
+
+
+def make_desc(q, k, v, o, *, causal: bool, q_pos0: int, scale, out_dtype, lse=None) -> ShattnDesc:
     if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("Q, K, V must share one dtype: bfloat16 or float32")
+    _check_shapes(q, k, v, o, lse)
     d = ShattnDesc()
     d.batch, d.heads_q, d.seq_q, d.head_dim = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
     d.heads_kv = k.shape[1]
@@ -152,7 +175,7 @@ def attn_chunk_fwd(q, k_chunk, v_chunk, *, kv_pos0: int, causal: bool = False, q
             or not lse_part.is_contiguous():
         raise ValueError("o_part/lse_part must be float32 (lse_part contiguous)")
     desc = make_desc(q, k_chunk, v_chunk, o_part, causal=causal, q_pos0=q_pos0, scale=scale,
-                     out_dtype=torch.float32)
+                     out_dtype=torch.float32, lse=lse_part)
     lib = load_library()
     st = lib.attn_chunk_fwd(ctypes.byref(desc), q.data_ptr(), k_chunk.data_ptr(),
                             v_chunk.data_ptr(), k_chunk.shape[2], int(kv_pos0),
@@ -169,7 +192,10 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part):
             raise ValueError("lse_merge takes contiguous float32 tensors")
     dim = o_acc.shape[-1]
     rows = lse_acc.numel()
-    if o_acc.numel() != rows * dim or o_part.numel() != rows * dim or lse_part.numel() != rows:
+    if o_part.shape != o_acc.shape or lse_part.shape != lse_acc.shape \
+            or tuple(o_acc.shape[:-1]) != tuple(lse_acc.shape):
+        raise ValueError("O tensors must share one shape [..., D] and LSE tensors its [...]")
+    if o_acc.numel() != rows * dim:
         raise ValueError("shape mismatch between O and LSE tensors")
     st = load_library().lse_merge(rows, dim, o_acc.data_ptr(), lse_acc.data_ptr(),
                                   o_part.data_ptr(), lse_part.data_ptr(), _stream(o_acc))
@@ -195,7 +221,7 @@ def attn_shifted_fwd(q, k, v, *, num_chunks: int, rank: int, causal: bool = Fals
     if out.dtype != out_dtype or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("bad output tensors")
     desc = make_desc(q, k, v, out, causal=causal, q_pos0=q_pos0, scale=scale,
-                     out_dtype=out_dtype)
+                     out_dtype=out_dtype, lse=lse)
     st = load_library().attn_shifted_fwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(),
                                          v.data_ptr(), k.shape[2], int(num_chunks), int(rank),
                                          out.data_ptr(), lse.data_ptr(), _stream(q))
@@ -230,7 +256,7 @@ def attn_shifted_fwd_overlapped(q, k_src, v_src, k, v, *, num_chunks: int, rank:
     if copy_stream is None:
         copy_stream = torch.cuda.Stream(device=q.device)
     desc = make_desc(q, k, v, o, causal=causal, q_pos0=q_pos0, scale=scale,
-                     out_dtype=torch.float32)
+                     out_dtype=torch.float32, lse=lse)
     st = load_library().attn_shifted_fwd_overlapped(
         ctypes.byref(desc), q.data_ptr(), k_src.data_ptr(), v_src.data_ptr(), k.data_ptr(),
         v.data_ptr(), k.shape[2], int(num_chunks), int(rank), o.data_ptr(), lse.data_ptr(),

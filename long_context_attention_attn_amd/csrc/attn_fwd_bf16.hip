@@ -81,6 +81,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kernels.h"
 
 namespace shattn {
@@ -105,8 +107,11 @@ constexpr int kTileBytes = kTile * 2;
 constexpr int kRing = 4;              // LDS ring depth per stream
 // The reference max of a row moves (which needs the accumulated O and l
 // rescaled) only when a score exceeds it by more than this, in log2 units.
-// Until then p <= 2^64: with |v| < 2^40 and < 2^31 keys, O and l stay far
-// below the fp32 range, and fp32 / bf16 keep full relative precision.
+// Until then every p <= 2^64, so with n visible keys the row sum stays below
+// n * 2^64 and each unnormalised output element below n * 2^64 * max|v|.
+// fp32 overflows at 2^128: results are finite while max|v| * n < 2^64 (for
+// example |v| < 2^33 at the 2^31-row limit of a call).  A running max would
+// allow max|v| * n up to 2^128; the header states the narrower range.
 constexpr float kRescaleSlack = 64.0f;
 static_assert(kBlockM == kWaves * 64, "64 query rows per wave");
 
@@ -1149,17 +1154,19 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   }  // items
 }
 
-// Compute units of the current device (one resident block each).
+// Compute units of the current device (one resident block each).  The
+// per-device cache is filled with relaxed atomic stores of the same value, so
+// first calls racing from several host threads are well defined.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <typename TOut>

@@ -109,6 +109,39 @@ def test_property_weights_rows_sum_to_one(causal):
         assert (w[kp[None, :] > qp[:, None]] == 0).all()
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_weights_are_the_weights_attention_uses(causal):
+    """Binds the rows-sum-to-one property to the oracle's own attention:
+
+    * the weights equal torch's float64 softmax of the masked, scaled scores
+      (a library routine; a dropped or wrong scale fails here);
+    * they equal exp(scale q.k - LSE) with LSE from :func:`oracle.attention`;
+    * W @ V equals :func:`oracle.attention`'s O for a V of full column rank
+      (19 keys, head_dim 32), which fixes W uniquely: they are exactly the
+      weights the monolithic attention applies, and those rows sum to 1.
+    """
+    n, m, d, scale = 11, 19, 32, 0.37
+    q, k, v = _rand((n, d), 21, 2.0), _rand((m, d), 22, 2.0), _rand((m, d), 23)
+    qp = 6 + np.arange(n)
+    kp = np.arange(m)
+    w = oracle.softmax_weights(q, k, qp, kp, causal=causal, scale=scale)
+    s = torch.from_numpy(scale * (q @ k.T))
+    if causal:
+        s = s.masked_fill(torch.from_numpy(kp[None, :] > qp[:, None]), float("-inf"))
+    np.testing.assert_allclose(w, torch.softmax(s, dim=1).numpy(), atol=1e-14, rtol=0)
+    o, lse = oracle.attention(q[None, None], k[None, None], v[None, None], causal=causal,
+                              q_pos0=int(qp[0]), scale=scale)
+    w_lse = np.exp(scale * (q @ k.T) - lse[0, 0][:, None])
+    if causal:
+        w_lse = np.where(kp[None, :] <= qp[:, None], w_lse, 0.0)
+    np.testing.assert_allclose(w, w_lse, atol=1e-13, rtol=0)
+    assert np.linalg.matrix_rank(v) == m
+    np.testing.assert_allclose(w @ v, o[0, 0], atol=1e-12, rtol=0)
+    # The weights recovered from attention's own output sum to one per row.
+    w_attn = o[0, 0] @ np.linalg.pinv(v)
+    np.testing.assert_allclose(w_attn.sum(axis=1), 1.0, atol=1e-10, rtol=0)
+
+
 def _merge_case(causal, q_pos0, skv=24, hq=4, hkv=2, seed=10):
     q = _rand((2, hq, 9, 8), seed, 2.0)
     k = _rand((2, hkv, skv, 8), seed + 1, 2.0)
