@@ -23,7 +23,13 @@
  *  - Every argument is validated on the host before anything is launched; on
  *    failure the call returns a non-zero status and launches nothing.  No
  *    exceptions cross this boundary and nothing aborts.
- *  - NaN/Inf in inputs propagate to the outputs; they are never masked.
+ *  - NaN/Inf in inputs propagate to the outputs; they are never masked.  In
+ *    the bf16 path they can also reach a few rows that do not see them:
+ *    with a NaN/Inf in V, the rows of a 64-row query group that reads the
+ *    64-key tile holding it get NaN in that column (0 * NaN in P V); with a
+ *    NaN/Inf score (from Q or K), query t +- 16 of t's 32-row block gets a
+ *    NaN output row (the sum of rounded probabilities that divides O is
+ *    taken for both rows in one matrix op).  LSE is unaffected by either.
  *  - Range (bf16 inputs): the softmax keeps a per-row reference that moves
  *    only when a score exceeds it by more than 64 in log2 units, so an
  *    unnormalised output element can reach n * 2^64 * max|v| for a row with

@@ -341,6 +341,28 @@ __device__ __forceinline__ void pv_mfma(f32x16& o, const bf16x8& a, const bf16x8
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
+// Row sums of the bf16-rounded probabilities, on the matrix cores.  O is
+// divided by the sum of the very weights P V multiplied (the fp32 sum of the
+// unrounded values gives the LSE): every output is then an exact convex
+// combination of V rows, and the bf16 rounding of p_k moves it by
+// sum_k w_k d_k (v_k - O) rather than sum_k w_k d_k v_k (d_k the relative
+// rounding error), so rows dominated by a few keys keep their values.
+// One 16x16x32 op per query block and 16-key step: A is a constant 0/1
+// pattern, B the P^T operand of the 32x32x16 P V op.  Read with the 16x16x32
+// layout (lane l: column l % 16, keys 8 * (l / 16) .. + 7), lanes c and c + 32
+// hold query c's 16 keys and lanes c + 16, c + 48 query c + 16's; A row 0 is
+// one on key groups 0 and 2, row 1 on groups 1 and 3.  Result: lane c < 16
+// holds query c's sum in register 0 and query c + 16's in register 1
+// (accumulated in fp32 over the whole walk; every other element stays 0).
+// Adding the rounded values with vector instructions instead would cost
+// four more per probability pair in a loop whose vector issue is the limit.
+// The zeros of A still multiply the other query's probabilities: a
+// non-finite probability of query t (from a NaN or Inf in Q or K) also makes
+// the sum, hence the output row, of query t +- 16 of its 32-row block NaN.
+__device__ __forceinline__ void psum_mfma(f32x4& acc, const bf16x8& ones, const bf16x8& p) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "a"(ones), "v"(p));
+}
+
 // O and Q^T live in AGPRs.  Reading or rescaling O goes through a VGPR
 // copy made by these empty statements, so that O itself is never used by a
 // vector ALU instruction: otherwise the compiler keeps O in VGPRs and copies
@@ -403,6 +425,33 @@ __device__ __forceinline__ float lane_swap32_max(float x) {
 __device__ __forceinline__ float lane_swap32_add(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wait states for the matrix ops writing acc to retire, as an asm statement
+// that names acc: no read of it can be scheduled ahead of the wait.
+__device__ __forceinline__ void settle_acc(f32x4& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc) : : "memory");
+}
+
+// Scales the rounded-P sums of a query block by a per-query factor f (lane
+// l holds query l % 32's): lane c < 16 keeps query c in register 0 and query
+// c + 16 in register 1.
+__device__ __forceinline__ void scale_lr(f32x4& acc, float f) {
+  const float f16 = __shfl_down(f, 16);
+  settle_acc(acc);
+  f32x4 t = agpr_get(acc);
+  t[0] *= f;
+  t[1] *= f16;
+  agpr_set(acc, t);
+}
+
+// The rounded-P sum of this lane's query (l % 32), from psum_mfma's layout.
+__device__ __forceinline__ float lr_total(f32x4& acc, int lq) {
+  settle_acc(acc);
+  const f32x4 t = agpr_get(acc);
+  const float a = __shfl(t[0], lq & 15);
+  const float b = __shfl(t[1], lq & 15);
+  return lq < 16 ? a : b;
 }
 
 template <typename TOut>
@@ -616,7 +665,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   // slack - m_use is far (-inf before the first tile, which so always
   // takes the rare branch).
   float t_far[2];
-  float l_run[2];            // this lane's half of the row sums
+  float l_run[2];            // this lane's half of the row sums (fp32 p: the LSE)
+  // Sums of the rounded P (divide O), see psum_mfma; and its constant A.
+  f32x4 lr[2];
+  bf16x8 ones;
   // P^T operands: pb[qb][ks] holds keys 16*ks .. 16*ks+15 of the tile being
   // multiplied into O (ks 0-1: key block 0, ks 2-3: key block 1).
   bf16x8 pb[2][4];
@@ -627,6 +679,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], (f32x16){});
+    agpr_set(lr[qb], (f32x4){0.f, 0.f, 0.f, 0.f});
     m_ref[qb] = -INFINITY;
     m_use[qb] = 0.f;
     t_far[qb] = -INFINITY;
@@ -639,6 +692,14 @@ void attn_fwd_bf16_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][qb][r] = -INFINITY;
+  }
+  {
+    const int row = lane & 15, grp = lane >> 4;
+    const bool one = (row == 0 && (grp & 1) == 0) || (row == 1 && (grp & 1) == 1);
+    bf16x8 t;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) t[x] = (__bf16)(one ? 1.0f : 0.0f);
+    agpr_set(ones, t);
   }
   // The compiler must not know P's starting value: a known constant gets
   // rebuilt by vector moves right in front of the asm matrix ops, which do
@@ -813,9 +874,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       va[n % 4] = read_v_at(voff[n & 3] + v_slot_off, n >> 2);
       if (!(st & 1)) asm volatile("" : : "v"(va[(st + 1) % 4]));
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
+      if ((st & 3) == 3) psum_mfma(lr[0], ones, pb[0][st >> 2]);
       scale_max_kb1(2 * st);
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
+      if ((st & 3) == 3) psum_mfma(lr[1], ones, pb[1][st >> 2]);
       scale_max_kb1(2 * st + 1);
       if (st == 0) {
         // Tile j-1's sums join the row sums.
@@ -886,9 +949,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       }
       if (!(st & 1)) asm volatile("" : : "v"(va[(st + 1) % 4]));
       pv_mfma(o[0][st & 3], va[st % 4], pb[0][st >> 2]);
+      if ((st & 3) == 3) psum_mfma(lr[0], ones, pb[0][st >> 2]);
       exp_job(2 * st);
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(o[1][st & 3], va[st % 4], pb[1][st >> 2]);
+      if ((st & 3) == 3) psum_mfma(lr[1], ones, pb[1][st >> 2]);
       exp_job(2 * st + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -898,9 +963,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       // Rare: tile j-1's P V (old scale) is complete once its ops retire.
       matrix_settle();
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) agpr_set(o[qb][db], agpr_get(o[qb][db]) * o_scale[qb]);
+        scale_lr(lr[qb], o_scale[qb]);
+      }
     }
     {
       v_row = k_row;
@@ -967,6 +1034,10 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       if (st + 2 < 16) va[(st + 2) % 3] = read_v(vrel, voff, (st + 2) >> 2, (st + 2) & 3);
       pv_mfma(o[0][st & 3], va[st % 3], pb[0][st >> 2]);
       pv_mfma(o[1][st & 3], va[st % 3], pb[1][st >> 2]);
+      if ((st & 3) == 3) {
+        psum_mfma(lr[0], ones, pb[0][st >> 2]);
+        psum_mfma(lr[1], ones, pb[1][st >> 2]);
+      }
     }
   }
 
@@ -1054,6 +1125,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
           __builtin_amdgcn_sched_barrier(0);
           agpr_set(o[qb][db], agpr_get(o[qb][db]) * alpha[qb]);
         }
+        scale_lr(lr[qb], alpha[qb]);
       }
     };
     auto qk_phase = [&](int qb, auto&& extra) {
@@ -1080,6 +1152,7 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         if (st + 2 < 16) va[(st + 2) % 3] = read_v(vrel, voff, (st + 2) >> 2, (st + 2) & 3);
         pv_mfma(o[qb][st & 3], va[st % 3], pb[qb][st >> 2]);
+        if ((st & 3) == 3) psum_mfma(lr[qb], ones, pb[qb][st >> 2]);
         extra(st);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1097,8 +1170,9 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   }
 
   matrix_settle();
-  // Finalise: O = acc / l, LSE = (m_ref + log2 l) ln 2; l == 0 means no
-  // visible key (O = 0, LSE = -inf).  NaN in l propagates.
+  // Finalise: O = acc / (sum of the rounded P it was built from), LSE =
+  // (m_ref + log2 l) ln 2 with l the fp32 sum; l == 0 means no visible key
+  // (O = 0, LSE = -inf).  NaN in l propagates.
   // bf16 output goes through LDS: each wave stages its 32-row blocks in its
   // own 16 KiB of the K ring (every wave is past its last tile once the
   // barrier below is passed), so that the stores write whole rows, 16 bytes
@@ -1110,8 +1184,9 @@ void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = lane_swap32_add(l_run[qb]);
+    const float l_rnd = lr_total(lr[qb], lq);
     const bool empty = l_tot == 0.f;
-    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float inv = empty ? 0.f : 1.f / l_rnd;
     const float lse = empty ? -INFINITY : (m_ref[qb] + __log2f(l_tot)) * 0.69314718055994530942f;
     const int64_t my_q = wave_q0 + 32 * qb + lq;
     if (kStaged) {
