@@ -29,7 +29,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "BY_NAME", "slice_seed", "gen_qkv", "make_inputs"]
+__all__ = ["Workload", "WORKLOADS", "BY_NAME", "slice_seed", "gen_qkv", "make_inputs",
+           "GemmWorkload", "GEMM_WORKLOADS", "GEMM_BY_NAME", "gen_gemm", "make_gemm_inputs"]
 
 
 @dataclass(frozen=True)
@@ -184,3 +185,77 @@ def make_inputs(w: Workload, device="cpu"):
                    seq_kv=w.seq_kv, head_dim=w.head_dim, dtype=w.torch_dtype,
                    device=device, seed=w.index, std=w.std, heavy_frac=w.heavy_frac,
                    heavy_mult=w.heavy_mult)
+
+
+# ---------------------------------------------------------------------------
+# Shifted all-gather GEMM: one rank's share of a tensor-parallel projection.
+# The activation A [M, K] is sharded by rows over J ranks and gathered; the
+# rank's weight shard W [N, K] (column-parallel, out x in) is local; the rank
+# consumes A's row chunks in the order (j + rank) % J and computes
+# C = A W^T [M, N].  The pages measure this pattern as the all-gather GEMM at
+# batch 16 (Silicon & Systems digest of Mercury, "What Mercury finds that
+# templates miss").
+#
+# Input recipe (a reading; the pages give none): A ~ N(0, 1) (activations),
+# W ~ N(0, 1) / sqrt(K) (so C ~ N(0, 1)), each drawn in float32 from its own
+# seeded generator, seed (workload << 40) + (tensor << 32) + chunk with
+# tensor A = 0 (one generator per row chunk), W = 1, then rounded to bf16.
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    """One shifted all-gather GEMM call: C [M, N] = A [M, K] W [N, K]^T."""
+
+    index: int
+    name: str
+    m: int
+    n: int
+    k: int
+    num_chunks: int
+    rank: int
+    summary: str = field(default="", compare=False)
+
+    @property
+    def chunk_rows(self) -> int:
+        return self.m // self.num_chunks
+
+    def visit_order(self):
+        return [(j + self.rank) % self.num_chunks for j in range(self.num_chunks)]
+
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+    def min_bytes(self) -> int:
+        """A + W read once, C written once (bf16 everywhere)."""
+        return 2 * (self.m * self.k + self.n * self.k + self.m * self.n)
+
+
+GEMM_WORKLOADS = (
+    GemmWorkload(100, "gemm_tiny_ragged", 1000, 200, 256, 4, 1,
+                 summary="1000 x 256 activation in 4 chunks of 250 rows, 200 outputs: "
+                         "ragged against every tile size"),
+    GemmWorkload(101, "llama3_8b_tp8_mlp_b16", 32768, 3584, 4096, 8, 3,
+                 summary="Llama-3-8B-like MLP gate+up projection, tensor parallel over 8 "
+                         "GPUs: batch 16 x 2048 tokens gathered from 8 row chunks, the "
+                         "rank's 3584-column weight shard (2 x 14336 / 8), rank 3"),
+)
+
+GEMM_BY_NAME = {w.name: w for w in GEMM_WORKLOADS}
+
+
+def gen_gemm(*, m: int, n: int, k: int, num_chunks: int, device="cpu", seed: int = 0):
+    """Seeded A [M, K] (one generator per row chunk) and W [N, K], bf16."""
+    dev = torch.device(device)
+    a = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    clen = -(-m // num_chunks)
+    for c in range(num_chunks):
+        r0, r1 = c * clen, min(m, (c + 1) * clen)
+        if r1 > r0:
+            a[r0:r1] = _randn((r1 - r0, k), slice_seed(seed, 0, 0, c), dev).to(torch.bfloat16)
+    w = (_randn((n, k), slice_seed(seed, 1, 0, 0), dev) / math.sqrt(k)).to(torch.bfloat16)
+    return a, w
+
+
+def make_gemm_inputs(w: GemmWorkload, device="cpu"):
+    return gen_gemm(m=w.m, n=w.n, k=w.k, num_chunks=w.num_chunks, device=device, seed=w.index)

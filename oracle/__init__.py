@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for shifted-chunk attention (test infrastructure only).
+"""fp64 CPU oracle for shifted-chunk attention and the shifted all-gather
+GEMM (test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 leg may import this package.  It shares no code with the HIP library.
@@ -13,3 +14,4 @@ from .attention_fp64 import (  # noqa: F401
     shifted_attention,
     softmax_weights,
 )
+from .gemm_fp64 import gemm, gemm_rows, shifted_allgather_gemm  # noqa: F401
