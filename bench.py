@@ -37,8 +37,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (AMD's "2.5 PFLOP/s" dense)
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["long_context_attention_attn_amd/csrc/attn_fwd_bf16.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_{workload}_traffic.json")
+# The kernel that dominates each kind of workload: its source (whose hash
+# tags a traffic summary) and the name prefix rocprofv3 reports for it.
+KERNELS = {
+    "attn": ("long_context_attention_attn_amd/csrc/attn_fwd_bf16.hip", "attn_fwd"),
+    "gemm": ("long_context_attention_attn_amd/csrc/gemm_bf16.hip", "gemm_bf16"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "{prefix}_{workload}_traffic.json")
 # torch's negation kernel serves as the calibration copy: it reads and writes
 # each element once.
 CALIB_KERNEL = "neg_kernel"
@@ -49,23 +54,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def kernel_kind(workload: str) -> str:
+    from long_context_attention_attn_amd.workloads import GEMM_BY_NAME
+
+    return "gemm" if workload in GEMM_BY_NAME else "attn"
+
+
+def kernel_hash(kind: str = "attn") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    with open(os.path.join(ROOT, KERNELS[kind][0]), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     it is missing or was taken on a different kernel source."""
-    path = TRAFFIC_FILE.format(workload=workload)
+    kind = kernel_kind(workload)
+    path = TRAFFIC_FILE.format(prefix=KERNELS[kind][1], workload=workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha") != kernel_hash():
+    if rec.get("kernel_sha") != kernel_hash(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -171,8 +182,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, workload: str, copy_
             raise SystemExit(f"no {counter} rows for a kernel matching {needle!r} under {root}")
         return sum(sums.values()) / len(sums) * 1024.0, len(sums)
 
-    f_attn, n_fa = per_dispatch(fetch_dir, "FETCH_SIZE", "attn_fwd")
-    w_attn, n_wa = per_dispatch(write_dir, "WRITE_SIZE", "attn_fwd")
+    kind = kernel_kind(workload)
+    prefix = KERNELS[kind][1]
+    f_attn, n_fa = per_dispatch(fetch_dir, "FETCH_SIZE", prefix)
+    w_attn, n_wa = per_dispatch(write_dir, "WRITE_SIZE", prefix)
     f_copy, _ = per_dispatch(fetch_dir, "FETCH_SIZE", CALIB_KERNEL)
     w_copy, _ = per_dispatch(write_dir, "WRITE_SIZE", CALIB_KERNEL)
     copy_bytes = copy_mib * 2**20
@@ -180,7 +193,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out: str, workload: str, copy_
     w_scale = copy_bytes / w_copy
     rec = {
         "workload": workload,
-        "kernel_sha": kernel_hash(),
+        "kernel": prefix,
+        "kernel_sha": kernel_hash(kind),
         "dispatches": [n_fa, n_wa],
         "fetch_bytes_raw": f_attn,
         "write_bytes_raw": w_attn,
@@ -326,6 +340,110 @@ def merge_report(w, steps: int, warmup: int):
     return 0
 
 
+def gemm_report(wl, steps: int, warmup: int, cpu_seconds: float, no_cpu: bool):
+    """One JSON line for the shifted all-gather GEMM workload ``wl``: C = A W^T
+    with A's row chunks visited from chunk ``rank`` on, inputs resident.
+    Beside it, torch's own bf16 matmul of the same operands (the vendor
+    library) is timed on the same stream, as context."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from long_context_attention_attn_amd import binding
+    from long_context_attention_attn_amd.workloads import make_gemm_inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"bench: gemm workload {wl.name}: generating inputs")
+    a, w = make_gemm_inputs(wl, dev)
+    c = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.allgather_gemm_shifted(a, w, num_chunks=wl.num_chunks, rank=wl.rank, out=c)
+
+    def timed(fn, n_warm, n_steps):
+        for _ in range(n_warm):
+            fn()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+        for i in range(n_steps):
+            evs[i].record(stream)
+            fn()
+        evs[-1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(x.elapsed_time(y) for x, y in zip(evs[:-1], evs[1:]))
+        return evs[0].elapsed_time(evs[-1]) / max(n_steps, 1), per
+
+    log(f"bench: warmup {warmup}, timing {steps} steps")
+    ms, per = timed(step, warmup, steps)
+    flops = wl.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"bench: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
+    wt = w.t()
+    ms_lib, _ = timed(lambda: torch.matmul(a, wt, out=c), max(3, warmup // 5), max(5, steps // 2))
+    rec = {
+        "metric": "shifted all-gather GEMM TFLOP/s per MI355X + % bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": wl.name, "m": wl.m, "n": wl.n, "k": wl.k,
+                   "num_chunks": wl.num_chunks, "rank": wl.rank,
+                   "algorithmic_gflop": round(flops / 1e9, 3),
+                   "parallelism": "one rank's share on 1 GPU"},
+        "launch_ms": {"mean": round(ms, 5), "median": round(per[len(per) // 2], 5),
+                      "min": round(per[0], 5), "max": round(per[-1], 5)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(wl.name)},
+        "context": {"torch_matmul_ms": round(ms_lib, 5),
+                    "torch_matmul_tflops": round(flops / (ms_lib * 1e-3) / 1e12, 1)},
+    }
+    if not no_cpu:
+        log(f"bench: cpu baseline (fp64 oracle, ~{cpu_seconds:.0f} s)")
+        cores = len(os.sched_getaffinity(0))
+        try:
+            from threadpoolctl import threadpool_limits
+
+            limiter = threadpool_limits(limits=cores)
+        except Exception:  # pragma: no cover
+            limiter = None
+        w64 = w.cpu().double().numpy()
+        rows_done, elapsed, prep = 0, 0.0, 0.0
+        block = 1024
+        while elapsed < cpu_seconds and rows_done < wl.m:
+            r1 = min(wl.m, rows_done + block)
+            t0 = time.perf_counter()
+            a64 = a[rows_done:r1].cpu().double().numpy()
+            t1 = time.perf_counter()
+            oracle.gemm(a64, w64)
+            t2 = time.perf_counter()
+            prep += t1 - t0
+            elapsed += t2 - t1
+            rows_done = r1
+        blas = _blas_info()
+        if limiter is not None:
+            limiter.restore_original_limits()
+        rec["cpu_baseline"] = {
+            "value": 2 * rows_done * wl.n * wl.k / elapsed / 1e12,
+            "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_done} of {wl.m} rows of A, fp64 numpy; oracle {elapsed:.1f} s, "
+                      f"host copy + fp64 upcast {prep:.1f} s (not in the rate)",
+            "blas": blas, "oracle_s": round(elapsed, 2), "upcast_s": round(prep, 2)}
+    del np
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,6 +477,11 @@ def main():
     from long_context_attention_attn_amd import binding
     from long_context_attention_attn_amd.workloads import BY_NAME, make_inputs
 
+    from long_context_attention_attn_amd.workloads import GEMM_BY_NAME
+
+    if args.workload in GEMM_BY_NAME:
+        return gemm_report(GEMM_BY_NAME[args.workload], args.steps, args.warmup,
+                           args.cpu_seconds, args.no_cpu_baseline)
     w = BY_NAME[args.workload]
     if args.lse_merge:
         return merge_report(w, args.steps, args.warmup)

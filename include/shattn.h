@@ -193,6 +193,46 @@ SHATTN_API int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* 
                                 float* o, float* lse, float* o_part, float* lse_part,
                                 hipStream_t compute_stream, hipStream_t copy_stream);
 
+/*
+ * Shifted all-gather GEMM: one rank's share of a tensor-parallel product
+ * whose shared operand stays sharded and is consumed piece by piece in a
+ * rank-staggered order (Silicon & Systems digest of Mercury, section "The
+ * hidden cost of synchronized operators": each rank owns a slice of one
+ * matrix, all ranks need the other, and the schedule shifts the order in
+ * which ranks consume the shared buffer; measured as the all-gather GEMM in
+ * section "What Mercury finds that templates miss").  The shift order is
+ * CommIR's (j + i) % J (papers.lqhl.me summary, section 核心方法).
+ *
+ * A [m, k]: the gathered activation, bf16, row-major (row stride lda
+ * elements); its rows form num_chunks equal chunks, chunk c being rows
+ * [c*m/J, (c+1)*m/J) (the piece rank c holds).  W [n, k]: the rank's weight
+ * shard, bf16, row-major out x in (row stride ldw).  C [m, n] = A W^T,
+ * row-major (row stride ldc), in out_dtype (bf16 rounded to nearest even
+ * from the fp32 accumulator, or fp32).  Chunks are visited in the order
+ * c_j = (j + rank) % num_chunks: output tiles of chunk c_j are started
+ * before those of c_{j+1}.  The result does not depend on the order.
+ */
+typedef struct {
+  int64_t m, n, k;       /* C [m, n] = A [m, k] W [n, k]^T; k == 0 writes zeros */
+  int64_t lda, ldw, ldc; /* row strides in elements (>= k, k, n)             */
+  int32_t out_dtype;     /* shattn_dtype of C                                */
+} shattn_gemm_desc;
+
+/*
+ * allgather_gemm_shifted — C = A W^T in one launch, A's chunks visited from
+ * chunk `rank` on.
+ *
+ * Requirements: 0 <= rank < num_chunks; m a multiple of num_chunks; k a
+ * multiple of 64 and n of 8 (else SHATTN_EUNSUPPORTED); lda, ldw multiples
+ * of 8 and ldc of 8 (bf16 C) or 4 (fp32 C); a, w, c 16-byte aligned; lda,
+ * ldw at most 2^22 (SHATTN_EUNSUPPORTED beyond).  m == 0 or n == 0 is a
+ * successful no-op.  Pointers are device memory owned by the caller; the
+ * call enqueues one kernel on `stream` and allocates nothing.
+ */
+SHATTN_API int allgather_gemm_shifted(const shattn_gemm_desc* desc, const void* a, const void* w,
+                                      void* c, int32_t num_chunks, int32_t rank,
+                                      hipStream_t stream);
+
 /* attn_status_string — static, NUL-terminated name of a status code. */
 SHATTN_API const char* attn_status_string(int status);
 

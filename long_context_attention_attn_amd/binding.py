@@ -23,6 +23,8 @@ __all__ = [
     "attn_shifted_fwd",
     "attn_shifted_fwd_overlapped",
     "attn_status_string",
+    "allgather_gemm_shifted",
+    "ShattnGemmDesc",
     "DTYPE_CODES",
 ]
 
@@ -60,6 +62,20 @@ class ShattnDesc(ctypes.Structure):
     ]
 
 
+class ShattnGemmDesc(ctypes.Structure):
+    """Mirror of ``shattn_gemm_desc``."""
+
+    _fields_ = [
+        ("m", ctypes.c_int64),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("lda", ctypes.c_int64),
+        ("ldw", ctypes.c_int64),
+        ("ldc", ctypes.c_int64),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
 _LIB = None
 
 
@@ -88,6 +104,9 @@ def load_library():
     lib.attn_shifted_fwd_overlapped.argtypes = [dp, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp,
                                                 vp, vp, vp, vp]
     lib.attn_shifted_fwd_overlapped.restype = ctypes.c_int
+    lib.allgather_gemm_shifted.argtypes = [ctypes.POINTER(ShattnGemmDesc), vp, vp, vp, i32, i32,
+                                           vp]
+    lib.allgather_gemm_shifted.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -267,3 +286,44 @@ def attn_shifted_fwd_overlapped(q, k_src, v_src, k, v, *, num_chunks: int, rank:
     # device K/V are ordered by the current stream, which ends after the
     # copies.
     return o, lse
+
+
+def _row_stride(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major matrix (contiguous rows)")
+    return t.stride(0)
+
+
+def allgather_gemm_shifted(a, w, *, num_chunks: int, rank: int, out_dtype=None, out=None):
+    """C = A W^T with A's row chunks visited from chunk ``rank`` on.
+
+    ``a`` [M, K] bf16 (the gathered activation, M a multiple of
+    ``num_chunks``), ``w`` [N, K] bf16 (the rank's weight shard).  Returns C
+    [M, N] in ``out_dtype`` (default bf16) or into ``out``.
+    """
+    _require_cuda(a, w, out)
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("A and W must be bfloat16")
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError(f"A {tuple(a.shape)} and W {tuple(w.shape)} must be [M, K] and [N, K]")
+    m, k = a.shape
+    n = w.shape[0]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out_dtype not in DTYPE_CODES:
+        raise ValueError("C must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if out.dtype != out_dtype or tuple(out.shape) != (m, n):
+        raise ValueError(f"C must be [M, N] = {(m, n)} of {out_dtype}")
+    d = ShattnGemmDesc()
+    d.m, d.n, d.k = m, n, k
+    d.lda, d.ldw, d.ldc = _row_stride(a, "A"), _row_stride(w, "W"), _row_stride(out, "C")
+    if k == 0:  # an empty contraction has no rows to step over
+        d.lda = d.ldw = 0
+    d.out_dtype = DTYPE_CODES[out_dtype]
+    st = load_library().allgather_gemm_shifted(ctypes.byref(d), a.data_ptr(), w.data_ptr(),
+                                               out.data_ptr(), int(num_chunks), int(rank),
+                                               _stream(a))
+    _check("allgather_gemm_shifted", st)
+    return out

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libshattn.so")
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "lse_merge.hip", "shattn_api.cpp"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "lse_merge.hip", "gemm_bf16.hip",
+           "shattn_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code.

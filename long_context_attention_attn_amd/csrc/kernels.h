@@ -56,4 +56,22 @@ hipError_t launch_attn_fwd_f32(const FwdParams& p, DType out, hipStream_t stream
 hipError_t launch_lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse_acc,
                             const float* o_part, const float* lse_part, hipStream_t stream);
 
+// One rank's share of the shifted all-gather GEMM: C [m, n] = A [m, k] W [n, k]^T,
+// A's rows in num_chunks chunks of chunk_rows visited (j + rank) % num_chunks.
+// Row strides in elements; k a multiple of 64, n of 8.
+struct GemmParams {
+  const void* a;
+  const void* w;
+  void* c;
+  int64_t m, n, k;
+  int64_t lda, ldw, ldc;
+  int64_t chunk_rows;
+  int32_t num_chunks, rank;
+  int32_t tiles_per_chunk;  // ceil(chunk_rows / 256)
+  int32_t n_tiles_m;        // num_chunks * tiles_per_chunk
+  int32_t n_tiles_n;        // ceil(n / 256)
+};
+
+hipError_t launch_gemm_bf16(const GemmParams& p, DType out, hipStream_t stream);
+
 }  // namespace shattn

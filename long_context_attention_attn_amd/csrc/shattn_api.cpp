@@ -315,6 +315,51 @@ int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q, const vo
   return SHATTN_OK;
 }
 
+int allgather_gemm_shifted(const shattn_gemm_desc* desc, const void* a, const void* w, void* c,
+                           int32_t num_chunks, int32_t rank, hipStream_t stream) {
+  if (desc == nullptr) return SHATTN_EINVAL;
+  const shattn_gemm_desc& d = *desc;
+  if (num_chunks < 1 || rank < 0 || rank >= num_chunks) return SHATTN_EINVAL;
+  if (d.m < 0 || d.n < 0 || d.k < 0 || d.m > kPosLimit || d.n > kPosLimit || d.k > kPosLimit)
+    return SHATTN_EINVAL;
+  if (d.m % num_chunks != 0) return SHATTN_EINVAL;
+  if (!valid_dtype(d.out_dtype)) return SHATTN_EINVAL;
+  if (d.k % 64 != 0 || d.n % 8 != 0) return SHATTN_EUNSUPPORTED;
+  const bool empty = d.m == 0 || d.n == 0;
+  if (!empty && (a == nullptr && d.k > 0)) return SHATTN_EINVAL;
+  if (!empty && ((w == nullptr && d.k > 0) || c == nullptr)) return SHATTN_EINVAL;
+  if (d.lda < d.k || d.ldw < d.k || d.ldc < d.n) return SHATTN_EINVAL;
+  if (d.lda % 8 != 0 || d.ldw % 8 != 0 || d.ldc % (d.out_dtype == SHATTN_F32 ? 4 : 8) != 0)
+    return SHATTN_EINVAL;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return SHATTN_EINVAL;
+  // A tile's copies address up to 256 rows in 32-bit byte offsets.
+  if (d.lda > kSeqStrideLimit / 4 || d.ldw > kSeqStrideLimit / 4) return SHATTN_EUNSUPPORTED;
+  const int64_t chunk_rows = d.m / num_chunks;
+  const int64_t tiles_per_chunk = (chunk_rows + 255) / 256;
+  const int64_t tiles_m = tiles_per_chunk * num_chunks;
+  const int64_t tiles_n = (d.n + 255) / 256;
+  if (tiles_m > INT32_MAX / 8 || ((tiles_m + 7) / 8) * 8 * tiles_n > INT32_MAX)
+    return SHATTN_EUNSUPPORTED;
+  if (empty) return SHATTN_OK;
+  shattn::GemmParams p = {};
+  p.a = a;
+  p.w = w;
+  p.c = c;
+  p.m = d.m;
+  p.n = d.n;
+  p.k = d.k;
+  p.lda = d.lda;
+  p.ldw = d.ldw;
+  p.ldc = d.ldc;
+  p.chunk_rows = chunk_rows;
+  p.num_chunks = num_chunks;
+  p.rank = rank;
+  p.tiles_per_chunk = (int32_t)tiles_per_chunk;
+  p.n_tiles_m = (int32_t)tiles_m;
+  p.n_tiles_n = (int32_t)tiles_n;
+  return status_of(shattn::launch_gemm_bf16(p, (DType)d.out_dtype, stream));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case SHATTN_OK:

@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
     assert set(names) == {"attn_chunk_fwd", "lse_merge", "attn_shifted_fwd",
-                          "attn_shifted_fwd_overlapped", "attn_status_string"}
+                          "attn_shifted_fwd_overlapped", "allgather_gemm_shifted",
+                          "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -198,3 +199,62 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding.attn_shifted_fwd(q, q, q, num_chunks=1, rank=0)
+
+
+def _gdesc(**over):
+    d = binding.ShattnGemmDesc()
+    d.m, d.n, d.k = 1024, 256, 512
+    d.lda, d.ldw, d.ldc = 512, 512, 256
+    d.out_dtype = binding.BF16
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def _gemm(lib, d, a=FAKE, w=FAKE, c=FAKE, nch=4, rank=1):
+    return lib.allgather_gemm_shifted(ctypes.byref(d) if d is not None else None, a, w, c, nch,
+                                      rank, None)
+
+
+def test_gemm_desc_layout():
+    assert ctypes.sizeof(binding.ShattnGemmDesc) == 6 * 8 + 8
+    assert binding.ShattnGemmDesc.out_dtype.offset == 48
+
+
+@pytest.mark.parametrize("case,expect", [
+    ({"m": -1}, 1),
+    ({"n": -8}, 1),
+    ({"k": -64}, 1),
+    ({"m": 1001}, 1),             # not a multiple of the chunk count
+    ({"k": 96}, 2),               # valid, not built (k % 64)
+    ({"n": 100, "ldc": 104}, 2),  # valid, not built (n % 8)
+    ({"lda": 256}, 1),            # row stride below k
+    ({"ldw": 500}, 1),
+    ({"ldc": 200}, 1),
+    ({"lda": 516}, 1),            # not a multiple of 8 elements
+    ({"ldc": 260}, 1),            # bf16 C rows must stay 16-byte aligned
+    ({"out_dtype": 5}, 1),
+    ({"lda": (1 << 22) + 8}, 2),  # 32-bit tile addressing
+])
+def test_gemm_rejects_bad_desc(case, expect):
+    lib = _lib()
+    assert _gemm(lib, _gdesc(**case)) == expect
+
+
+def test_gemm_rejects_bad_arguments():
+    lib = _lib()
+    d = _gdesc()
+    assert _gemm(lib, None) == 1
+    assert _gemm(lib, d, rank=4) == 1
+    assert _gemm(lib, d, rank=-1) == 1
+    assert _gemm(lib, d, nch=0) == 1
+    assert _gemm(lib, d, a=0) == 1
+    assert _gemm(lib, d, w=0) == 1
+    assert _gemm(lib, d, c=0) == 1
+    assert _gemm(lib, d, a=FAKE + 2) == 1
+    assert _gemm(lib, d, c=FAKE + 8) == 1
+    # fp32 C: a row stride of 260 floats (1040 bytes) is 16-byte aligned.
+    assert _gemm(lib, _gdesc(out_dtype=binding.F32, ldc=260, n=256), a=0, nch=4) == 1
+    # Nothing to compute: a no-op that touches no pointer.
+    assert _gemm(lib, _gdesc(m=0), a=0, w=0, c=0) == 0
+    assert _gemm(lib, _gdesc(n=0, ldc=0), a=0, w=0, c=0) == 0

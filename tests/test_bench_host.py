@@ -23,7 +23,7 @@ def test_traffic_is_reported_only_for_the_kernel_it_was_measured_on(tmp_path, mo
     rec = {"workload": "w", "kernel_sha": bench.kernel_hash(), "hbm_bytes_per_launch": 123.0}
     path = tmp_path / "attn_fwd_w_traffic.json"
     path.write_text(json.dumps(rec))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "attn_fwd_{workload}_traffic.json"))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "{prefix}_{workload}_traffic.json"))
     assert bench.read_traffic("w") == 123.0
     rec["kernel_sha"] = "0" * 16
     path.write_text(json.dumps(rec))
@@ -42,4 +42,4 @@ def test_committed_traffic_files_name_their_kernel():
         # The read-back agrees with the hash check, whichever way it goes.
         w = rec["workload"]
         got = bench.read_traffic(w)
-        assert (got is not None) == (rec["kernel_sha"] == bench.kernel_hash())
+        assert (got is not None) == (rec["kernel_sha"] == bench.kernel_hash(bench.kernel_kind(w)))

@@ -1,0 +1,116 @@
+"""GPU parity of the shifted all-gather GEMM (through the C ABI) against the
+fp64 oracle.
+
+Tolerance, derived from the arithmetic (the pages state none for the GEMM):
+bf16 products are exact in fp32, so the fp32 result differs from the exact
+sum only by fp32 accumulation rounding, at most about k * 2^-24 of
+sum_k |a_mk| |w_nk|; with k <= 4096 that is below 2^-12 of it, the bound
+used.  A bf16 output adds one rounding of C, at most 2^-8 |C|.  The bf16
+output must also equal the fp32 output rounded to bf16, bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_attention_attn_amd import binding
+from long_context_attention_attn_amd.workloads import GEMM_BY_NAME, gen_gemm, make_gemm_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check(c32, c16, a, w, rows=None):
+    """Element-wise bound check of fp32 and bf16 C (selected rows or all)."""
+    a64 = a.double().cpu().numpy()
+    w64 = w.double().cpu().numpy()
+    if rows is not None:
+        a64 = a64[rows]
+        c32 = c32[torch.as_tensor(rows, device=c32.device)]
+        c16 = c16[torch.as_tensor(rows, device=c16.device)]
+    ref = a64 @ w64.T
+    bound = 2.0 ** -12 * (np.abs(a64) @ np.abs(w64).T)
+    g32 = c32.double().cpu().numpy()
+    g16 = c16.double().cpu().numpy()
+    e32 = np.abs(g32 - ref)
+    e16 = np.abs(g16 - ref)
+    assert (e32 <= bound).all(), f"fp32 C: max excess {float(np.max(e32 - bound))}"
+    assert (e16 <= bound + 2.0 ** -8 * np.abs(ref)).all(), "bf16 C beyond its bound"
+    return float(e32.max()), float(e16.max())
+
+
+def _run(a, w, nch, rank):
+    c32 = binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=rank, out_dtype=torch.float32)
+    c16 = binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=rank)
+    torch.cuda.synchronize()
+    assert torch.equal(c32.to(torch.bfloat16), c16)
+    return c32, c16
+
+
+@pytest.mark.parametrize("m,n,k,nch,rank", [
+    (256, 256, 64, 1, 0),        # one tile, one K step
+    (512, 512, 128, 2, 1),       # 2 x 2 tiles, 2 steps
+    (1000, 200, 256, 4, 1),      # chunks of 250 rows: ragged rows and columns
+    (96, 8, 64, 3, 2),           # tiny chunks, one 8-column piece
+    (4 * 300, 520, 192, 4, 3),   # ragged row tiles per chunk, 3 column tiles
+    (2048, 1024, 512, 8, 5),     # more row tiles than XCDs
+])
+def test_small_shapes_full(m, n, k, nch, rank):
+    a, w = gen_gemm(m=m, n=n, k=k, num_chunks=nch, device=DEV, seed=m + n + k)
+    c32, c16 = _run(a, w, nch, rank)
+    ref = oracle.shifted_allgather_gemm(a.cpu(), w.cpu(), num_chunks=nch, rank=rank)
+    np.testing.assert_array_equal(ref, oracle.gemm(a.cpu(), w.cpu()))
+    _check(c32, c16, a, w)
+
+
+def test_every_rank_same_result():
+    """The visit order changes which tiles start first, never the values:
+    every rank's launch gives the same C, bit for bit."""
+    m, n, k, nch = 8 * 256, 512, 256, 8
+    a, w = gen_gemm(m=m, n=n, k=k, num_chunks=nch, device=DEV, seed=7)
+    outs = [binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=r, out_dtype=torch.float32)
+            for r in range(nch)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    _check(outs[0], outs[0].to(torch.bfloat16), a, w)
+
+
+def test_strided_operands():
+    """Row strides above K and N (views into wider buffers)."""
+    m, n, k, nch = 600, 264, 128, 2
+    a_big, w_big = gen_gemm(m=m, n=n, k=k + 64, num_chunks=nch, device=DEV, seed=11)
+    a, w = a_big[:, 32:32 + k], w_big[:, 64:64 + k]
+    out_big = torch.empty((m, n + 40), dtype=torch.float32, device=DEV)
+    c32 = binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=1, out=out_big[:, :n])
+    torch.cuda.synchronize()
+    _check(c32, c32.to(torch.bfloat16), a, w)
+
+
+def test_zero_k_writes_zeros():
+    a = torch.empty((64, 0), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty((16, 0), dtype=torch.bfloat16, device=DEV)
+    c = torch.full((64, 16), 7.0, dtype=torch.float32, device=DEV)
+    binding.allgather_gemm_shifted(a, w, num_chunks=2, rank=1, out=c)
+    torch.cuda.synchronize()
+    assert bool((c == 0).all())
+
+
+@pytest.mark.parametrize("name", ["gemm_tiny_ragged", "llama3_8b_tp8_mlp_b16"])
+def test_workload_every_element(name):
+    """Each GEMM workload at its full size, in the benchmark's launch
+    configuration, every element against the oracle."""
+    wl = GEMM_BY_NAME[name]
+    a, w = make_gemm_inputs(wl, DEV)
+    c32, c16 = _run(a, w, wl.num_chunks, wl.rank)
+    e32, e16 = _check(c32, c16, a, w)
+    print(f"gemm parity {name}: max |dC| fp32 out {e32:.3e}, bf16 out {e16:.3e}", flush=True)
+
+
+def test_deterministic():
+    a, w = gen_gemm(m=1024, n=512, k=512, num_chunks=4, device=DEV, seed=3)
+    outs = [binding.allgather_gemm_shifted(a, w, num_chunks=4, rank=2) for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
