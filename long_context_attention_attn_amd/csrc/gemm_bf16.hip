@@ -25,13 +25,15 @@
 // row l % 32 of the block, columns 8 g + 4 (l / 32) .. + 3 in registers
 // 4 g .. 4 g + 3, written as 8- or 16-byte pieces of C's rows.
 //
-// Data movement.  K advances 64 at a time through a 2-deep LDS ring per
-// operand (global_load_lds_dwordx4 straight from global memory, 16 KB per
-// 64 rows of 128 bytes).  16-byte chunks are XOR-swizzled by (row >> 1) & 7
-// so that the operand reads (one 16-byte chunk per lane, 32 rows by 2
-// chunks per wave) meet no bank conflicts.  A step runs 4 k-substeps of 16
-// matrix ops with the next step's copies spread among them; one barrier per
-// step.
+// Data movement.  K advances 32 at a time through a 5-deep LDS ring per
+// operand (global_load_lds_dwordx4 straight from global memory; a slot is
+// 256 rows of 64 bytes, 16 KB; the two rings fill the 160 KB of LDS), so the
+// copies of a step are issued four steps (about 4 K cycles) before it runs:
+// with one wave per SIMD nothing else hides the memory latency.  16-byte
+// chunks are XOR-swizzled by (row >> 2) & 3 so that the operand reads (one
+// 16-byte chunk per lane, 32 rows by 2 chunks per wave) meet no bank
+// conflicts.  A step runs 2 k-substeps of 16 matrix ops with the copies of
+// step + 4 spread among the second; one barrier per step, between them.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,19 +51,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
-constexpr int kTileK = 64;                    // K per ring slot
-constexpr int kRowBytes = kTileK * 2;         // 128 bytes per operand row in LDS
-constexpr int kSlotBytes = 256 * kRowBytes;   // 32 KB per operand per slot
+constexpr int kTileK = 32;                    // K per ring slot
+constexpr int kRowBytes = kTileK * 2;         // 64 bytes per operand row in LDS
+constexpr int kSlotBytes = 256 * kRowBytes;   // 16 KB per operand per slot
+constexpr int kStages = 5;                    // ring depth
+constexpr int kSubsteps = kTileK / 16;        // matrix-op k-steps per slot
+constexpr int kCopies = 8;                    // 1 KB copies per wave per step
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
 }
 
-// Physical 16-byte chunk of logical chunk c in row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Physical 16-byte chunk of logical chunk c in row r (an involution).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// One 1 KB global->LDS copy: 8 rows of 128 bytes.  M0 holds the LDS
+// One 1 KB global->LDS copy: 16 rows of 64 bytes.  M0 holds the LDS
 // destination, the source is an SGPR base plus a per-lane byte offset.  As
 // inline assembly the compiler does not make later LDS reads wait for it;
 // the kernel waits explicitly before the barrier that publishes a slot.
@@ -82,13 +87,20 @@ __device__ __forceinline__ const void* uniform(const void* p) {
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ void wait_copies_all() { __builtin_amdgcn_s_waitcnt(0xF70); }
+// Waits until at most 24 (16) of this wave's copies are in flight.
+__device__ __forceinline__ void wait_copies_24() { __builtin_amdgcn_s_waitcnt(0x4F78); }
+__device__ __forceinline__ void wait_copies_16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+
+// Workgroup barrier; the wave's own LDS reads are complete before it arrives.
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <typename TOut>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) char lds_a[2][kSlotBytes];
-  __shared__ __attribute__((aligned(16))) char lds_w[2][kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char lds_a[kStages][kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char lds_w[kStages][kSlotBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,41 +123,41 @@ void gemm_bf16_kernel(GemmParams p) {
   const int64_t col0 = (int64_t)nt * kTileN;
   const int cols = (int)min((int64_t)kTileN, p.n - col0);
 
-  // Copies: wave w fills rows 64 w .. 64 w + 63 of both operand slots, 8 per
-  // instruction; lane i writes LDS row 8 n + i / 8, physical chunk i % 8,
-  // which holds logical chunk swz(row, i % 8) (an involution).  Rows past the
-  // tile's end copy its last row (their results are never stored).
+  // Copies: wave w fills rows 64 w .. 64 w + 63 of both operand slots, 16
+  // per instruction; lane i writes LDS row 16 n + i / 4, physical chunk
+  // i % 4, which holds logical chunk swz(row, i % 4).  Rows past the tile's
+  // end copy its last row (their results are never stored).
   const __bf16* abase = (const __bf16*)p.a + row0 * p.lda;
   const __bf16* wbase = (const __bf16*)p.w + col0 * p.ldw;
   const uint32_t lda_b = (uint32_t)(p.lda * 2), ldw_b = (uint32_t)(p.ldw * 2);
-  uint32_t a_off[8], w_off[8];
+  uint32_t a_off[4], w_off[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int r = 64 * wave + 8 * n + (lane >> 3);
-    const int c = swz(r, lane & 7);
+  for (int n = 0; n < 4; ++n) {
+    const int r = 64 * wave + 16 * n + (lane >> 2);
+    const int c = swz(r, lane & 3);
     a_off[n] = (uint32_t)min(r, rows - 1) * lda_b + (uint32_t)c * 16u;
     w_off[n] = (uint32_t)min(r, cols - 1) * ldw_b + (uint32_t)c * 16u;
   }
   const uint32_t a_dst0 = lds_addr(&lds_a[0][0]) + (uint32_t)(64 * wave) * kRowBytes;
   const uint32_t w_dst0 = lds_addr(&lds_w[0][0]) + (uint32_t)(64 * wave) * kRowBytes;
-  // Copy instruction n (0..15: A rows, then W rows) of K-step ks into a slot.
+  // Copy instruction n (0..7: A rows, then W rows) of K-step ks into a slot.
   auto copy_n = [&](int ks, int slot, int n) {
-    if (n < 8)
+    if (n < 4)
       copy_1k(a_dst0 + (uint32_t)slot * kSlotBytes + 1024u * n,
               uniform(abase + (int64_t)ks * kTileK), a_off[n]);
     else
-      copy_1k(w_dst0 + (uint32_t)slot * kSlotBytes + 1024u * (n - 8),
-              uniform(wbase + (int64_t)ks * kTileK), w_off[n - 8]);
+      copy_1k(w_dst0 + (uint32_t)slot * kSlotBytes + 1024u * (n - 4),
+              uniform(wbase + (int64_t)ks * kTileK), w_off[n - 4]);
   };
 
   // Operand reads: block b of this wave, k-substep kk: row 32 b + lane % 32
   // of the wave's 128 rows, logical chunk 2 kk + lane / 32.
   const int wm = wave >> 1, wn = wave & 1;
-  int rd_off[4][4];  // [block][kk] byte offset within a slot (same for A and W rows)
+  int rd_off[4][kSubsteps];  // [block][kk] byte offset within a slot (A and W alike)
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < kSubsteps; ++kk) {
       const int r = 32 * b + (lane & 31);
       rd_off[b][kk] = r * kRowBytes + swz(r, 2 * kk + (lane >> 5)) * 16;
     }
@@ -158,56 +170,79 @@ void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) acc[i][jj] = (f32x16){};
 
-  // K loop.  Step ks: wait for this wave's copies of the step (issued during
-  // the step before), barrier (every wave's copies are in; nobody reads the
-  // other slot any more), then 4 k-substeps of 16 matrix ops, each
-  // substep's operands read one substep ahead, and the 16 copies of step
-  // ks + 1 into the other slot spread over the step, two after every 8 ops.
+  // K loop.  Step ks sits in slot ks % 5 and runs 2 k-substeps of 16 matrix
+  // ops.  The barrier sits between them: once this wave's copies of step
+  // ks + 1 are in (the two later steps' copies may still fly), a barrier
+  // makes everyone's visible and frees the slot of step ks - 1 (every wave is
+  // past its reads).  After it the wave issues the copies of step ks + 4
+  // into that slot, one after every 2 ops of the second substep, and reads
+  // step ks + 1's first operands, so that the next step starts on operands
+  // already in registers.  Operands are read one substep ahead throughout.
+  // Past the last step the copies repeat it into slots nothing reads, so
+  // every step issues the same copies and the wait counts stay constant.
   const int nk = (int)(p.k / kTileK);
+  bf16x8 av[2][4], wv[2][4];
   if (nk > 0) {
 #pragma unroll
-    for (int n = 0; n < 16; ++n) copy_n(0, 0, n);
-  }
-  for (int ks = 0; ks < nk; ++ks) {
-    const int slot = ks & 1;
-    const bool more = ks + 1 < nk;
-    wait_copies_all();
-    __syncthreads();
-    const char* ab = a_rd + slot * kSlotBytes;
-    const char* wb = w_rd + slot * kSlotBytes;
-    bf16x8 av[2][4], wv[2][4];
+    for (int st = 0; st < kStages - 1; ++st)
+#pragma unroll
+      for (int n = 0; n < kCopies; ++n) copy_n(min(st, nk - 1), st, n);
+    wait_copies_24();
+    barrier();
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      av[0][b] = *(const bf16x8*)(ab + rd_off[b][0]);
-      wv[0][b] = *(const bf16x8*)(wb + rd_off[b][0]);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1;
-      if (kk < 3) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          av[cur ^ 1][b] = *(const bf16x8*)(ab + rd_off[b][kk + 1]);
-          wv[cur ^ 1][b] = *(const bf16x8*)(wb + rd_off[b][kk + 1]);
-        }
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2 * half; i < 2 * half + 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[cur][jj], av[cur][i],
-                                                                 acc[i][jj], 0, 0, 0);
-        if (more) {
-          copy_n(ks + 1, slot ^ 1, 4 * kk + 2 * half);
-          copy_n(ks + 1, slot ^ 1, 4 * kk + 2 * half + 1);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      av[0][b] = *(const bf16x8*)(a_rd + rd_off[b][0]);
+      wv[0][b] = *(const bf16x8*)(w_rd + rd_off[b][0]);
     }
   }
+  int slot = 0;
+  for (int ks = 0; ks < nk; ++ks) {
+    const int fill = slot == 0 ? kStages - 1 : slot - 1;
+    const int next = slot == kStages - 1 ? 0 : slot + 1;
+    const int ks_fill = min(ks + kStages - 1, nk - 1);
+    const char* ab = a_rd + slot * kSlotBytes;
+    const char* wb = w_rd + slot * kSlotBytes;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      av[1][b] = *(const bf16x8*)(ab + rd_off[b][1]);
+      wv[1][b] = *(const bf16x8*)(wb + rd_off[b][1]);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        acc[q4][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[0][jj], av[0][q4],
+                                                              acc[q4][jj], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_copies_16();
+    barrier();
+    if (ks + 1 < nk) {
+      const char* an = a_rd + next * kSlotBytes;
+      const char* wn = w_rd + next * kSlotBytes;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        av[0][b] = *(const bf16x8*)(an + rd_off[b][0]);
+        wv[0][b] = *(const bf16x8*)(wn + rd_off[b][0]);
+      }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        acc[q4][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[1][jj], av[1][q4],
+                                                              acc[q4][jj], 0, 0, 0);
+        if (jj & 1) copy_n(ks_fill, fill, 2 * q4 + (jj >> 1));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    slot = next;
+  }
+  // The repeated copies of the last steps land before the workgroup's LDS
+  // can be handed to another workgroup.
+  __builtin_amdgcn_s_waitcnt(0xF70);
 
   // Epilogue: C[row][col .. col + 3] from registers 4 g .. 4 g + 3 of block
   // (i, jj): row = 128 wm + 32 i + lane % 32, col = 128 wn + 32 jj + 8 g +
