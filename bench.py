@@ -214,9 +214,9 @@ def overlap_report(w, q, k, v, steps: int, warmup: int):
     """One JSON line on the overlapped chunk walk: apart from the rank's own
     chunk, K/V start in pinned host memory (standing in for the peers that
     hold the chunks) and each chunk is copied in while the chunks before it
-    compute.  Timed beside it on the
-    same stream: the same chunk walk with K/V already in HBM, and a plain
-    host-to-device copy of the same bytes."""
+    compute, each chunk's partial merged in its kernel.  Timed beside it on
+    the same stream: the same chunk walk with K/V already in HBM, the fused
+    one-launch walk, and a plain host-to-device copy of the same bytes."""
     import torch
 
     from long_context_attention_attn_amd import binding
@@ -238,7 +238,6 @@ def overlap_report(w, q, k, v, steps: int, warmup: int):
     seen = [c for c in w.visit_order() if not w.causal or c * clen <= q_last]
     o = torch.empty((w.batch, w.heads_q, w.seq_q, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((w.batch, w.heads_q, w.seq_q), dtype=torch.float32, device=dev)
-    o_p, lse_p = torch.empty_like(o), torch.empty_like(lse)
     es = k.element_size()
     fetched = [c for c in seen if c != w.rank]
     nbytes = 2 * w.batch * w.heads_kv * len(fetched) * clen * w.head_dim * es
@@ -254,11 +253,17 @@ def overlap_report(w, q, k, v, steps: int, warmup: int):
     def resident():
         for j, c in enumerate(seen):
             sl = slice(c * clen, (c + 1) * clen)
-            binding.attn_chunk_fwd(q, k[:, :, sl], v[:, :, sl], kv_pos0=c * clen,
-                                   causal=w.causal, q_pos0=w.q_pos0,
-                                   o_part=o if j == 0 else o_p, lse_part=lse if j == 0 else lse_p)
-            if j:
-                binding.lse_merge(o, lse, o_p, lse_p)
+            if j == 0:
+                binding.attn_chunk_fwd(q, k[:, :, sl], v[:, :, sl], kv_pos0=c * clen,
+                                       causal=w.causal, q_pos0=w.q_pos0, o_part=o, lse_part=lse)
+            else:
+                binding.attn_chunk_fwd_accumulate(q, k[:, :, sl], v[:, :, sl], o, lse,
+                                                  kv_pos0=c * clen, causal=w.causal,
+                                                  q_pos0=w.q_pos0)
+
+    def fused():
+        binding.attn_shifted_fwd(q, k, v, num_chunks=w.num_chunks, rank=w.rank, causal=w.causal,
+                                 q_pos0=w.q_pos0, out=o, lse=lse)
 
     def transfer():
         d_buf.copy_(h_buf, non_blocking=True)
@@ -281,6 +286,8 @@ def overlap_report(w, q, k, v, steps: int, warmup: int):
     ms_res = timed(resident)
     log("bench: transfer only")
     ms_tr = timed(transfer)
+    log("bench: fused walk (one launch)")
+    ms_fused = timed(fused)
     shorter = min(ms_res, ms_tr)
     hidden = (ms_res + ms_tr - ms_ov) / shorter if nbytes and shorter > 0 else None
     rec = {
@@ -293,6 +300,7 @@ def overlap_report(w, q, k, v, steps: int, warmup: int):
         "bytes_fetched": nbytes,
         "ms_overlapped": round(ms_ov, 4),
         "ms_compute_resident": round(ms_res, 4),
+        "ms_fused_resident": round(ms_fused, 4),
         "ms_transfer_only": round(ms_tr, 4),
         "transfer_GBps": round(nbytes / (ms_tr * 1e-3) / 1e9, 2) if nbytes else None,
         "tflops_overlapped": round(w.flops() / (ms_ov * 1e-3) / 1e12, 3),

@@ -113,6 +113,26 @@ SHATTN_API int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void
                    hipStream_t stream);
 
 /*
+ * attn_chunk_fwd_accumulate — attn_chunk_fwd merged into a running pair.
+ *
+ * The same partial as attn_chunk_fwd, merged in the kernel's epilogue into
+ * (o_acc, lse_acc) with lse_merge's arithmetic instead of being written out:
+ * (o_acc, lse_acc) <- merge((o_acc, lse_acc), (O_c, LSE_c)).  A chunk
+ * consumed this way is never written as a separate fp32 partial and merged
+ * by a second pass: the running result moves where it is needed (digest,
+ * section "The hidden cost of synchronized operators"; summary, section
+ * 核心方法).  o_acc is fp32, strided by desc->o_stride in fp32 elements;
+ * lse_acc fp32 contiguous [batch, heads_q, seq_q]; an accumulator row with
+ * LSE -inf is empty (its O must be 0).  A row with no visible key in the
+ * chunk keeps its accumulator (the merge identity).  Requirements as
+ * attn_chunk_fwd.  Calls that merge into the same rows must be ordered on
+ * one stream.
+ */
+SHATTN_API int attn_chunk_fwd_accumulate(const shattn_desc* desc, const void* q, const void* k,
+                                         const void* v, int64_t kv_len, int64_t kv_pos0,
+                                         float* o_acc, float* lse_acc, hipStream_t stream);
+
+/*
  * lse_merge — in place, row by row:
  *   (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))
  * with M = max(L_a, L_b), L = M + log(exp(L_a - M) + exp(L_b - M)),
@@ -167,17 +187,18 @@ SHATTN_API int attn_shifted_fwd(const shattn_desc* desc, const void* q, const vo
  * j = 1..J-1 and c = (j + rank) % num_chunks, the call enqueues on
  * copy_stream the copy of chunk c's rows of every (batch, KV head) slice,
  * and on compute_stream, behind an event on those copies, the partial of Q
- * against chunk c (attn_chunk_fwd) merged into (o, lse) (lse_merge): the
- * copy of each chunk runs while the chunks before it compute.  A causal
+ * against chunk c merged into (o, lse) in the kernel's epilogue
+ * (attn_chunk_fwd_accumulate): the copy of each chunk runs while the chunks
+ * before it compute, and no partial is written or merged separately.  A causal
  * chunk that starts after the last query's position is neither copied nor
  * computed (its rows of k, v are left as they were).
  *
  * Outputs: o, fp32, contiguous [batch, heads_q, seq_q, head_dim] (so
  * desc->o_stride must be the contiguous strides; desc->out_dtype is
- * ignored), and lse, fp32 [batch, heads_q, seq_q].  o_part, lse_part: the
- * caller's scratch of the same shapes for one chunk's partial.  None of the
- * four may overlap.  Results equal attn_chunk_fwd over the visited chunks
- * merged in visit order, which equals attn_shifted_fwd up to rounding.
+ * ignored), and lse, fp32 [batch, heads_q, seq_q], which must not overlap.
+ * Results equal attn_chunk_fwd over the first visited chunk followed by
+ * attn_chunk_fwd_accumulate over the others in visit order, which equals
+ * attn_shifted_fwd up to rounding.
  *
  * Streams: copy_stream first waits for the work already enqueued on
  * compute_stream (which may still read k, v); compute_stream ends after all
@@ -190,8 +211,8 @@ SHATTN_API int attn_shifted_fwd(const shattn_desc* desc, const void* q, const vo
 SHATTN_API int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q,
                                 const void* k_src, const void* v_src, void* k, void* v,
                                 int64_t kv_len_total, int32_t num_chunks, int32_t rank,
-                                float* o, float* lse, float* o_part, float* lse_part,
-                                hipStream_t compute_stream, hipStream_t copy_stream);
+                                float* o, float* lse, hipStream_t compute_stream,
+                                hipStream_t copy_stream);
 
 /*
  * Shifted all-gather GEMM: one rank's share of a tensor-parallel product

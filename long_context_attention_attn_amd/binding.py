@@ -19,6 +19,7 @@ __all__ = [
     "library_path",
     "load_library",
     "attn_chunk_fwd",
+    "attn_chunk_fwd_accumulate",
     "lse_merge",
     "attn_shifted_fwd",
     "attn_shifted_fwd_overlapped",
@@ -97,12 +98,14 @@ def load_library():
     dp = ctypes.POINTER(ShattnDesc)
     lib.attn_chunk_fwd.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp]
     lib.attn_chunk_fwd.restype = ctypes.c_int
+    lib.attn_chunk_fwd_accumulate.argtypes = [dp, vp, vp, vp, i64, i64, vp, vp, vp]
+    lib.attn_chunk_fwd_accumulate.restype = ctypes.c_int
     lib.lse_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp]
     lib.lse_merge.restype = ctypes.c_int
     lib.attn_shifted_fwd.argtypes = [dp, vp, vp, vp, i64, i32, i32, vp, vp, vp]
     lib.attn_shifted_fwd.restype = ctypes.c_int
     lib.attn_shifted_fwd_overlapped.argtypes = [dp, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp,
-                                                vp, vp, vp, vp]
+                                                vp, vp]
     lib.attn_shifted_fwd_overlapped.restype = ctypes.c_int
     lib.allgather_gemm_shifted.argtypes = [ctypes.POINTER(ShattnGemmDesc), vp, vp, vp, i32, i32,
                                            vp]
@@ -203,6 +206,23 @@ def attn_chunk_fwd(q, k_chunk, v_chunk, *, kv_pos0: int, causal: bool = False, q
     return o_part, lse_part
 
 
+def attn_chunk_fwd_accumulate(q, k_chunk, v_chunk, o_acc, lse_acc, *, kv_pos0: int,
+                              causal: bool = False, q_pos0: int = 0, scale=None):
+    """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), partial of ``q``
+    against one KV chunk at ``kv_pos0``), the merge done in the kernel."""
+    _require_cuda(q, k_chunk, v_chunk, o_acc, lse_acc)
+    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32 \
+            or not lse_acc.is_contiguous():
+        raise ValueError("o_acc/lse_acc must be float32 (lse_acc contiguous)")
+    desc = make_desc(q, k_chunk, v_chunk, o_acc, causal=causal, q_pos0=q_pos0, scale=scale,
+                     out_dtype=torch.float32, lse=lse_acc)
+    st = load_library().attn_chunk_fwd_accumulate(
+        ctypes.byref(desc), q.data_ptr(), k_chunk.data_ptr(), v_chunk.data_ptr(),
+        k_chunk.shape[2], int(kv_pos0), o_acc.data_ptr(), lse_acc.data_ptr(), _stream(q))
+    _check("attn_chunk_fwd_accumulate", st)
+    return o_acc, lse_acc
+
+
 def lse_merge(o_acc, lse_acc, o_part, lse_part):
     """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
     _require_cuda(o_acc, lse_acc, o_part, lse_part)
@@ -270,8 +290,6 @@ def attn_shifted_fwd_overlapped(q, k_src, v_src, k, v, *, num_chunks: int, rank:
         raise ValueError("K and V differ in length")
     o = torch.empty((b, hq, sq, dim), dtype=torch.float32, device=q.device)
     lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
-    o_part = torch.empty_like(o)
-    lse_part = torch.empty_like(lse)
     if copy_stream is None:
         copy_stream = torch.cuda.Stream(device=q.device)
     desc = make_desc(q, k, v, o, causal=causal, q_pos0=q_pos0, scale=scale,
@@ -279,12 +297,11 @@ def attn_shifted_fwd_overlapped(q, k_src, v_src, k, v, *, num_chunks: int, rank:
     st = load_library().attn_shifted_fwd_overlapped(
         ctypes.byref(desc), q.data_ptr(), k_src.data_ptr(), v_src.data_ptr(), k.data_ptr(),
         v.data_ptr(), k.shape[2], int(num_chunks), int(rank), o.data_ptr(), lse.data_ptr(),
-        o_part.data_ptr(), lse_part.data_ptr(), _stream(q), copy_stream.cuda_stream)
+        _stream(q), copy_stream.cuda_stream)
     _check("attn_shifted_fwd_overlapped", st)
     # The sources must stay alive until the current stream has passed this
-    # call's work (the caller's references do that); the scratch and the
-    # device K/V are ordered by the current stream, which ends after the
-    # copies.
+    # call's work (the caller's references do that); the device K/V are
+    # ordered by the current stream, which ends after the copies.
     return o, lse
 
 

@@ -1213,6 +1213,11 @@ void attn_fwd_bf16_kernel(FwdParams p) {
       if (hh == 0 && my_q < p.seq_q) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
     } else if (my_q < p.seq_q) {
       TOut* orow = (TOut*)p.o + b * p.o_sb + h * p.o_sh + my_q * p.o_ss;
+      float* lrow = p.lse + ((int64_t)b * p.heads_q + h) * p.seq_q + my_q;
+      // Accumulating (fp32 output only): merge into the running pair.
+      const bool acc_mode = sizeof(TOut) == 4 && p.accumulate != 0;
+      float wa = 0.f, wb = 1.f, lse_out = lse;
+      if (acc_mode) merge_weights(*lrow, lse, wa, wb, lse_out);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const f32x16 ov = agpr_get(o[qb][db]);
@@ -1220,10 +1225,15 @@ void attn_fwd_bf16_kernel(FwdParams p) {
         for (int gq = 0; gq < 4; ++gq) {
           f32x4 v = {ov[4 * gq] * inv, ov[4 * gq + 1] * inv, ov[4 * gq + 2] * inv,
                      ov[4 * gq + 3] * inv};
-          store4<TOut>(orow + db * 32 + 8 * gq + 4 * hh, v);
+          TOut* dst = orow + db * 32 + 8 * gq + 4 * hh;
+          if (acc_mode) {
+            const f32x4 old = *(const f32x4*)dst;
+            v = old * wa + v * wb;
+          }
+          store4<TOut>(dst, v);
         }
       }
-      if (hh == 0) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
+      if (hh == 0) *lrow = lse_out;
     }
   }
   }  // items

@@ -304,15 +304,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(FwdParams p) {
   const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
   if (row_ok) {
     TOut* orow = (TOut*)p.o + b * p.o_sb + h * p.o_sh + my_q * p.o_ss;
+    float* lrow = p.lse + ((int64_t)b * p.heads_q + h) * p.seq_q + my_q;
+    // Accumulating (fp32 output only): merge into the running pair.
+    const bool acc_mode = sizeof(TOut) == 4 && p.accumulate != 0;
+    float wa = 0.f, wb = 1.f, lse_out = lse;
+    if (acc_mode) merge_weights(*lrow, lse, wa, wb, lse_out);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         int d0 = db * 32 + 8 * g + 4 * hh;
-        store_row4<TOut>(orow + d0, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                         acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        float x0 = acc[db][4 * g] * inv, x1 = acc[db][4 * g + 1] * inv;
+        float x2 = acc[db][4 * g + 2] * inv, x3 = acc[db][4 * g + 3] * inv;
+        if (acc_mode) {
+          const float* old = (const float*)(orow + d0);
+          x0 = old[0] * wa + x0 * wb;
+          x1 = old[1] * wa + x1 * wb;
+          x2 = old[2] * wa + x2 * wb;
+          x3 = old[3] * wa + x3 * wb;
+        }
+        store_row4<TOut>(orow + d0, x0, x1, x2, x3);
       }
-    if (hh == 0) p.lse[((int64_t)b * p.heads_q + h) * p.seq_q + my_q] = lse;
+    if (hh == 0) *lrow = lse_out;
   }
 }
 

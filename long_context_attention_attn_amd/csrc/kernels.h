@@ -3,7 +3,7 @@
 
 #include <stdint.h>
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 namespace shattn {
 
@@ -37,7 +37,27 @@ struct FwdParams {
   int32_t kv_rows;
   int32_t seg_a0;
   int64_t q_rel0;
+  // With fp32 output only: merge the result into (o, lse), which hold a
+  // running (O, LSE) pair, instead of overwriting them (lse_merge's
+  // arithmetic, in the kernel's epilogue).
+  int32_t accumulate;
 };
+
+// Weights and LSE of the merge of (O_a, L_a) with (O_b, L_b):
+// O = wa O_a + wb O_b, L = lse; two empty sides (-inf) give wa = wb = 0 and
+// lse = -inf.  The same operations as the standalone merge kernel.
+__device__ __forceinline__ void merge_weights(float la, float lb, float& wa, float& wb,
+                                              float& lse) {
+  const float mx = fmaxf(la, lb);
+  const bool both_empty = (mx == -INFINITY);
+  const float ms = both_empty ? 0.f : mx;
+  const float ea = __expf(la - ms);
+  const float eb = __expf(lb - ms);
+  const float tot = ea + eb;
+  wa = both_empty ? 0.f : ea / tot;
+  wb = both_empty ? 0.f : eb / tot;
+  lse = both_empty ? -INFINITY : ms + __logf(tot);
+}
 
 enum class DType : int { BF16 = 0, F32 = 1 };
 

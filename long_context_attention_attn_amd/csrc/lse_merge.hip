@@ -36,17 +36,8 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
   const int64_t row = wave * rows_per_wave + r_local;
   if (r_local >= rows_per_wave || row >= rows) return;
 
-  const float la = lse_acc[row];
-  const float lb = lse_part[row];
-  const float mx = fmaxf(la, lb);
-  const bool both_empty = (mx == -INFINITY);
-  const float ms = both_empty ? 0.f : mx;
-  const float wa = __expf(la - ms);
-  const float wb = __expf(lb - ms);
-  const float tot = wa + wb;
-  const float ca = both_empty ? 0.f : wa / tot;
-  const float cb = both_empty ? 0.f : wb / tot;
-  const float lse = both_empty ? -INFINITY : ms + __logf(tot);
+  float ca, cb, lse;
+  merge_weights(lse_acc[row], lse_part[row], ca, cb, lse);
 
   const int64_t off = row * head_dim + c * 4;
   f32x4 a = *(const f32x4*)(o_acc + off);

@@ -117,15 +117,21 @@ FwdParams make_params(const shattn_desc* d, const void* q, const void* k, const 
 
 extern "C" {
 
-int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
-                   int64_t kv_len, int64_t kv_pos0, float* o_part, float* lse_part,
-                   hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// attn_chunk_fwd, writing (accumulate = 0) or merging into (accumulate = 1)
+// the fp32 pair (o, lse).
+int chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
+              int64_t kv_len, int64_t kv_pos0, float* o, float* lse, int accumulate,
+              hipStream_t stream) {
   if (kv_len < 0 || kv_len > kPosLimit || kv_pos0 < 0 || kv_pos0 > kPosLimit)
     return SHATTN_EINVAL;
-  int st = check_desc(desc, q, k, v, o_part, lse_part, kv_len, 4);
+  int st = check_desc(desc, q, k, v, o, lse, kv_len, 4);
   if (st != SHATTN_OK) return st;
   if (kv_len > kKvRowLimit) return SHATTN_EUNSUPPORTED;
-  FwdParams p = make_params(desc, q, k, v, o_part, lse_part);
+  FwdParams p = make_params(desc, q, k, v, o, lse);
   p.kv_pos0 = kv_pos0;
   p.chunk_len = kv_len;
   p.num_chunks = 1;
@@ -133,8 +139,25 @@ int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const 
   p.kv_rows = (int32_t)kv_len;
   p.seg_a0 = 0;
   p.q_rel0 = desc->q_pos0 - kv_pos0;
+  p.accumulate = accumulate;
   if (desc->batch == 0 || desc->seq_q == 0) return SHATTN_OK;
   return status_of(shattn::launch_attn_fwd(p, (DType)desc->in_dtype, DType::F32, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_chunk_fwd(const shattn_desc* desc, const void* q, const void* k, const void* v,
+                   int64_t kv_len, int64_t kv_pos0, float* o_part, float* lse_part,
+                   hipStream_t stream) {
+  return chunk_fwd(desc, q, k, v, kv_len, kv_pos0, o_part, lse_part, 0, stream);
+}
+
+int attn_chunk_fwd_accumulate(const shattn_desc* desc, const void* q, const void* k,
+                              const void* v, int64_t kv_len, int64_t kv_pos0, float* o_acc,
+                              float* lse_acc, hipStream_t stream) {
+  return chunk_fwd(desc, q, k, v, kv_len, kv_pos0, o_acc, lse_acc, 1, stream);
 }
 
 }  // extern "C"
@@ -199,8 +222,7 @@ int attn_shifted_fwd(const shattn_desc* desc, const void* q, const void* k, cons
 int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q, const void* k_src,
                                 const void* v_src, void* k, void* v, int64_t kv_len_total,
                                 int32_t num_chunks, int32_t rank, float* o, float* lse,
-                                float* o_part, float* lse_part, hipStream_t compute_stream,
-                                hipStream_t copy_stream) {
+                                hipStream_t compute_stream, hipStream_t copy_stream) {
   if (num_chunks < 1 || rank < 0 || rank >= num_chunks) return SHATTN_EINVAL;
   if (kv_len_total < 0 || kv_len_total > kPosLimit || kv_len_total % num_chunks != 0)
     return SHATTN_EINVAL;
@@ -215,23 +237,17 @@ int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q, const vo
   // Rows must not overlap: each chunk is copied row by row at most.
   if (desc->k_stride[2] < desc->head_dim || desc->v_stride[2] < desc->head_dim)
     return SHATTN_EINVAL;
-  // O and its partial are contiguous [B, Hq, Sq, D]: the merge runs over rows.
+  // O is contiguous [B, Hq, Sq, D] and must not overlap LSE.
   const int64_t dim = desc->head_dim;
   const int64_t rows = (int64_t)desc->batch * desc->heads_q * desc->seq_q;
   if (desc->o_stride[2] != dim || desc->o_stride[1] != desc->seq_q * dim ||
       desc->o_stride[0] != desc->heads_q * desc->seq_q * dim)
     return SHATTN_EINVAL;
   if (q_empty) return SHATTN_OK;
-  st = check_merge(rows, (int32_t)dim, o, lse, o_part, lse_part);
-  if (st != SHATTN_OK) return st;
-  // The chunk partials are written too: no two of the four outputs overlap.
   {
+    const uintptr_t oa = (uintptr_t)o, la = (uintptr_t)lse;
     const uintptr_t ob = (uintptr_t)rows * (uintptr_t)dim * 4u, lb = (uintptr_t)rows * 4u;
-    const uintptr_t a[4] = {(uintptr_t)o, (uintptr_t)lse, (uintptr_t)o_part, (uintptr_t)lse_part};
-    const uintptr_t n[4] = {ob, lb, ob, lb};
-    for (int i = 0; i < 4; ++i)
-      for (int j = i + 1; j < 4; ++j)
-        if (a[i] < a[j] + n[j] && a[j] < a[i] + n[i]) return SHATTN_EINVAL;
+    if (oa < la + lb && la < oa + ob) return SHATTN_EINVAL;
   }
 
   const int64_t es = elem_size(desc->in_dtype);
@@ -300,12 +316,10 @@ int attn_shifted_fwd_overlapped(const shattn_desc* desc, const void* q, const vo
       ok(hipEventDestroy(ev));
       if (e != hipSuccess) break;
     }
-    // Partial of Q against chunk c, merged into (o, lse) in visit order.
-    st = attn_chunk_fwd(desc, q, chunk_ptr(k, desc->k_stride, c), chunk_ptr(v, desc->v_stride, c),
-                        clen, c * clen, first ? o : o_part, first ? lse : lse_part,
-                        compute_stream);
-    if (st == SHATTN_OK && !first)
-      st = lse_merge(rows, (int32_t)dim, o, lse, o_part, lse_part, compute_stream);
+    // Partial of Q against chunk c: the first one written to (o, lse), each
+    // later one merged into them in the kernel's epilogue, in visit order.
+    st = chunk_fwd(desc, q, chunk_ptr(k, desc->k_stride, c), chunk_ptr(v, desc->v_stride, c),
+                   clen, c * clen, o, lse, first ? 0 : 1, compute_stream);
     if (st != SHATTN_OK) return st;
     first = false;
   }

@@ -33,7 +33,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert set(names) == {"attn_chunk_fwd", "lse_merge", "attn_shifted_fwd",
+    assert set(names) == {"attn_chunk_fwd", "attn_chunk_fwd_accumulate", "lse_merge",
+                          "attn_shifted_fwd",
                           "attn_shifted_fwd_overlapped", "allgather_gemm_shifted",
                           "attn_status_string"}
     for n in names:
@@ -128,6 +129,22 @@ def test_shifted_rejects_bad_arguments():
     assert _shifted(lib, d, total=(1 << 31) - 56, nch=8) == 2
 
 
+def test_chunk_accumulate_rejects_bad_arguments():
+    lib = _lib()
+    d = _desc()
+
+    def acc(dd, q=FAKE, k=FAKE, v=FAKE, kv_len=256, kv_pos0=0, o=FAKE, lse=FAKE):
+        return lib.attn_chunk_fwd_accumulate(ctypes.byref(dd) if dd is not None else None, q, k,
+                                             v, kv_len, kv_pos0, o, lse, None)
+
+    assert acc(None) == 1
+    assert acc(d, kv_len=-1) == 1
+    assert acc(d, o=0) == 1
+    assert acc(d, lse=FAKE + 2) == 1
+    assert acc(_desc(head_dim=64)) == 2
+    assert acc(_desc(o_stride=S3(6, 6, 6))) == 1
+
+
 def test_chunk_rejects_bad_arguments():
     lib = _lib()
     d = _desc()
@@ -146,9 +163,9 @@ S1, S2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)  # stream handles, nev
 
 
 def _overlapped(lib, d, q=FAKE, ksrc=FAKE, vsrc=FAKE, k=FAKE, v=FAKE, total=1024, nch=4, rank=1,
-                o=0x1000000, lse=0x2000000, op=0x3000000, lp=0x4000000, cs=S1, ps=S2):
+                o=0x1000000, lse=0x2000000, cs=S1, ps=S2):
     return lib.attn_shifted_fwd_overlapped(ctypes.byref(d) if d is not None else None, q, ksrc,
-                                           vsrc, k, v, total, nch, rank, o, lse, op, lp, cs, ps)
+                                           vsrc, k, v, total, nch, rank, o, lse, cs, ps)
 
 
 def test_overlapped_rejects_bad_arguments():
@@ -162,18 +179,17 @@ def test_overlapped_rejects_bad_arguments():
     assert _overlapped(lib, d, ksrc=0) == 1
     assert _overlapped(lib, d, vsrc=0) == 1
     assert _overlapped(lib, d, k=0) == 1
-    assert _overlapped(lib, d, op=0) == 1
-    assert _overlapped(lib, d, op=0x3000000 + 4) == 1           # misaligned partial
-    assert _overlapped(lib, d, op=0x1000000 + 4096) == 1        # partial inside O
-    assert _overlapped(lib, d, lp=0x3000000 + 64) == 1          # LSE partial inside O partial
-    assert _overlapped(lib, d, lse=0x4000000 + 4) == 1          # the two LSE buffers overlap
+    assert _overlapped(lib, d, o=0) == 1
+    assert _overlapped(lib, d, o=0x1000000 + 4) == 1            # misaligned O
+    assert _overlapped(lib, d, lse=0x1000000 + 4096) == 1       # LSE inside O
+    assert _overlapped(lib, d, lse=0x2000000 + 2) == 1          # misaligned LSE
     assert _overlapped(lib, _desc(o_stride=S3(2 * 4 * 256 * 128, 256 * 128, 128))) == 1
     assert _overlapped(lib, _desc(head_dim=64)) == 2
     assert _overlapped(lib, _desc(k_stride=S3(4 * 256 * 128, 256 * 128, 64))) == 1  # rows overlap
     assert _overlapped(lib, d, total=(1 << 31) - 56, nch=8) == 2
     # No query rows: nothing to do, nothing enqueued.
     empty = _desc(seq_q=0, o_stride=S3(0, 0, 128))
-    assert _overlapped(lib, empty, q=0, o=0, lse=0, op=0, lp=0) == 0
+    assert _overlapped(lib, empty, q=0, o=0, lse=0) == 0
 
 
 def test_merge_rejects_bad_arguments():

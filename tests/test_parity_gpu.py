@@ -132,6 +132,63 @@ def _heads_to_check(w, seed=0, max_pairs=16):
     return sorted(pairs)
 
 
+def _accumulated(q, k, v, nch, rank, causal, q_pos0, upto=None):
+    """attn_chunk_fwd on the first visited chunk, then attn_chunk_fwd_accumulate
+    on the others in visit order (the merge inside the kernel)."""
+    b, hq, sq, d = q.shape
+    clen = k.shape[2] // nch
+    o = torch.empty((b, hq, sq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    for j in range(nch if upto is None else upto):
+        c = (j + rank) % nch
+        kc, vc = k[:, :, c * clen:(c + 1) * clen], v[:, :, c * clen:(c + 1) * clen]
+        if j == 0:
+            binding.attn_chunk_fwd(q, kc, vc, kv_pos0=c * clen, causal=causal, q_pos0=q_pos0,
+                                   o_part=o, lse_part=lse)
+        else:
+            binding.attn_chunk_fwd_accumulate(q, kc, vc, o, lse, kv_pos0=c * clen, causal=causal,
+                                              q_pos0=q_pos0)
+    return o, lse
+
+
+@pytest.mark.parametrize("case", [
+    (2, 4, 2, 200, 320, 5, 3, True, 120, torch.bfloat16),
+    (1, 2, 2, 300, 300, 3, 0, True, 0, torch.bfloat16),
+    (1, 4, 1, 700, 2048, 8, 6, True, 1400, torch.bfloat16),
+    (2, 2, 2, 100, 96, 3, 1, False, 0, torch.float32),
+    (1, 4, 2, 150, 480, 6, 4, True, 330, torch.float32),
+], ids=lambda c: "x".join(str(v) for v in c[:9]))
+def test_chunk_accumulate_mode(case):
+    """attn_chunk_fwd_accumulate merges each chunk's partial into the running
+    (O, LSE) inside the kernel: after the first j chunks of the visit order it
+    equals the oracle's chunk partials merged in that order (lse_merge of
+    chunk_attention), for every j; and the full walk equals the walk that
+    writes each partial and merges it with lse_merge, to fp32 rounding."""
+    b, hq, hkv, sq, skv, nch, rank, causal, q_pos0, din = case
+    _say(f"chunk accumulate {case}")
+    q, k, v = gen_qkv(batch=b, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=din, device=DEV, seed=83)
+    clen = skv // nch
+    qc, kc_all, vc_all = q.cpu(), k.cpu(), v.cpu()
+    o_ref = np.zeros((b, hq, sq, 128))
+    l_ref = np.full((b, hq, sq), -np.inf)
+    for j in range(nch):
+        c = (j + rank) % nch
+        sl = slice(c * clen, (c + 1) * clen)
+        o_c, l_c = oracle.chunk_attention(qc, kc_all[:, :, sl], vc_all[:, :, sl],
+                                          kv_pos0=c * clen, causal=causal, q_pos0=q_pos0)
+        o_ref, l_ref = oracle.lse_merge(o_ref, l_ref, o_c, l_c)
+        if j in (0, 1, nch // 2, nch - 1):
+            o, lse = _accumulated(q, k, v, nch, rank, causal, q_pos0, upto=j + 1)
+            torch.cuda.synchronize()
+            assert _max_err(o, o_ref) <= TOL_O[din], j
+            _check_lse(lse, l_ref)
+    o_sep, lse_sep = _composed(q, k, v, nch, rank, causal, q_pos0)
+    torch.cuda.synchronize()
+    assert float((o - o_sep).abs().max()) <= 1e-6
+    assert float((lse - lse_sep).abs().max()) <= 1e-6
+
+
 def _composed(q, k, v, nch, rank, causal, q_pos0):
     """attn_chunk_fwd over each chunk in visit order, merged with lse_merge."""
     b, hq, sq, d = q.shape
@@ -220,6 +277,29 @@ def test_kv_sharded_partials_tree_merge(din):
     assert float((lse_lin - lse).abs().max()) <= 1e-5
 
 
+def _accumulated_visible(q, k, v, nch, rank, q_pos0):
+    """_accumulated over the causally visible chunks only, in visit order."""
+    b, hq, sq, d = q.shape
+    clen = k.shape[2] // nch
+    q_last = q_pos0 + sq - 1
+    o = torch.empty((b, hq, sq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    first = True
+    for j in range(nch):
+        c = (j + rank) % nch
+        if c * clen > q_last:
+            continue
+        kc, vc = k[:, :, c * clen:(c + 1) * clen], v[:, :, c * clen:(c + 1) * clen]
+        if first:
+            binding.attn_chunk_fwd(q, kc, vc, kv_pos0=c * clen, causal=True, q_pos0=q_pos0,
+                                   o_part=o, lse_part=lse)
+        else:
+            binding.attn_chunk_fwd_accumulate(q, kc, vc, o, lse, kv_pos0=c * clen, causal=True,
+                                              q_pos0=q_pos0)
+        first = False
+    return o, lse
+
+
 def _pinned_like(t, layout_bshd=False):
     """A pinned host copy of device tensor t with the same strides."""
     if layout_bshd:
@@ -241,7 +321,8 @@ def _pinned_like(t, layout_bshd=False):
 ], ids=lambda c: "x".join(str(v) for v in c[:9]) + "-" + c[10] + ("-bshd" if c[11] else ""))
 def test_overlapped_chunk_walk(case):
     """Chunks copied in visit order on a second stream while earlier chunks
-    compute: equal to the resident chunk-by-chunk walk, and to the oracle.
+    compute, each merged in the kernel: equal bit for bit to the same
+    chunk-by-chunk walk with K/V resident, and to the oracle.
     The device K/V start as NaN except for the rank's own chunk, so a chunk
     read before its copy landed, or a causally invisible chunk that was
     computed, would show up."""
@@ -274,8 +355,14 @@ def test_overlapped_chunk_walk(case):
             assert torch.equal(part, k[:, :, c * clen:(c + 1) * clen]), f"chunk {c} not copied"
         else:
             assert bool(torch.isnan(part).all()), f"invisible chunk {c} was copied"
-    o_res, lse_res = _composed(q, k, v, nch, rank, causal, q_pos0)
+    o_res, lse_res = _accumulated(q, k, v, nch, rank, causal, q_pos0)
     torch.cuda.synchronize()
+    if causal:  # chunks after the last query are skipped by the walk, not merged
+        q_last = q_pos0 + sq - 1
+        nvis = sum(1 for j in range(nch) if ((j + rank) % nch) * clen <= q_last)
+        if nvis < nch:
+            o_res, lse_res = _accumulated_visible(q, k, v, nch, rank, q_pos0)
+            torch.cuda.synchronize()
     assert torch.equal(o, o_res) and torch.equal(lse, lse_res)
     o_ref, lse_ref = oracle.shifted_attention(q.cpu(), k.cpu(), v.cpu(), num_chunks=nch,
                                               rank=rank, causal=causal, q_pos0=q_pos0)
