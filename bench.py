@@ -41,6 +41,7 @@ PEAK_HBM_GBS = 8000.0
 # tags a traffic summary) and the name prefix rocprofv3 reports for it.
 KERNELS = {
     "attn": ("long_context_attention_attn_amd/csrc/attn_fwd_bf16.hip", "attn_fwd"),
+    "attn_f32": ("long_context_attention_attn_amd/csrc/attn_fwd_f32.hip", "attn_fwd_f32"),
     "gemm": ("long_context_attention_attn_amd/csrc/gemm_bf16.hip", "gemm_bf16"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "{prefix}_{workload}_traffic.json")
@@ -55,9 +56,12 @@ def log(msg):
 
 
 def kernel_kind(workload: str) -> str:
-    from long_context_attention_attn_amd.workloads import GEMM_BY_NAME
+    from long_context_attention_attn_amd.workloads import BY_NAME, GEMM_BY_NAME
 
-    return "gemm" if workload in GEMM_BY_NAME else "attn"
+    if workload in GEMM_BY_NAME:
+        return "gemm"
+    wl = BY_NAME.get(workload)
+    return "attn_f32" if wl is not None and wl.dtype == "f32" else "attn"
 
 
 def kernel_hash(kind: str = "attn") -> str:
@@ -348,7 +352,22 @@ def merge_report(w, steps: int, warmup: int):
     return 0
 
 
-def gemm_report(wl, steps: int, warmup: int, cpu_seconds: float, no_cpu: bool):
+def calibration_copy(mib: int, dev):
+    """One launch of the calibration kernel (torch's negation) over ``mib``
+    MiB of fp32: it reads and writes each byte once, which fixes the scale
+    of the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.empty(mib * 2**20 // 4, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def gemm_report(wl, steps: int, warmup: int, cpu_seconds: float, no_cpu: bool,
+                calib_copy_mib: int = 0):
     """One JSON line for the shifted all-gather GEMM workload ``wl``: C = A W^T
     with A's row chunks visited from chunk ``rank`` on, inputs resident.
     Beside it, torch's own bf16 matmul of the same operands (the vendor
@@ -388,6 +407,8 @@ def gemm_report(wl, steps: int, warmup: int, cpu_seconds: float, no_cpu: bool):
     flops = wl.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s")
+    if calib_copy_mib:
+        calibration_copy(calib_copy_mib, dev)
     wt = w.t()
     ms_lib, _ = timed(lambda: torch.matmul(a, wt, out=c), max(3, warmup // 5), max(5, steps // 2))
     rec = {
@@ -489,7 +510,7 @@ def main():
 
     if args.workload in GEMM_BY_NAME:
         return gemm_report(GEMM_BY_NAME[args.workload], args.steps, args.warmup,
-                           args.cpu_seconds, args.no_cpu_baseline)
+                           args.cpu_seconds, args.no_cpu_baseline, args.calib_copy_mib)
     w = BY_NAME[args.workload]
     if args.lse_merge:
         return merge_report(w, args.steps, args.warmup)
@@ -547,12 +568,7 @@ def main():
     log(f"bench: {ms:.4f} ms/step ({t_wall:.3f} s wall), {tflops:.1f} TFLOP/s")
 
     if args.calib_copy_mib:
-        src = torch.empty(args.calib_copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
-        src.fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
+        calibration_copy(args.calib_copy_mib, dev)
 
     is_f32 = w.dtype == "f32"
     peak = PEAK_F32_TFLOPS if is_f32 else PEAK_BF16_TFLOPS
