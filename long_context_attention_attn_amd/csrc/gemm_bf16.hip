@@ -13,30 +13,39 @@
 //
 // Work split.  A workgroup (4 waves, one per SIMD) computes a 256 x 256 tile
 // of C; wave w owns rows 128 * (w >> 1) and columns 128 * (w & 1) of it, as
-// 4 x 4 blocks of 32 x 32 in accumulator registers.  Tiles never straddle a
+// 8 x 8 blocks of 16 x 16 in accumulator registers.  Tiles never straddle a
 // chunk: each chunk's rows are tiled on their own, and tiles are numbered in
 // visit order.  The hardware deals workgroups round-robin to the 8 XCDs;
 // XCD x takes the row tiles x, x + 8, ... of that order, each with all its
 // column tiles, so one XCD's L2 serves an A tile to every workgroup that
 // reads it.
 //
-// Matrix cores: v_mfma_f32_32x32x16_bf16 with A-operand = W rows and
-// B-operand = A rows, so each 32 x 32 result block is C^T: lane l holds C
-// row l % 32 of the block, columns 8 g + 4 (l / 32) .. + 3 in registers
-// 4 g .. 4 g + 3, written as 8- or 16-byte pieces of C's rows.
+// Matrix cores: v_mfma_f32_16x16x32_bf16 with A-operand = W rows and
+// B-operand = A rows, so each 16 x 16 result block is C^T: lane l holds C
+// row l % 16 of the block, columns 4 (l / 16) .. + 3.  On this chip the
+// engine clock is held down by power under a dense product, and the
+// 16 x 16 x 32 ops cost less energy per flop than 32 x 32 x 16 ones (a
+// quarter of the accumulator registers per op for half the flops): the same
+// loop with the larger ops ran at a clock about 12 % lower for the same
+// cycles.  The ops are inline assembly so that each accumulator stays in
+// one AGPR quad; with the compiler's builtin the register allocator moved
+// accumulators between registers around every op.
 //
 // Data movement.  K advances 32 at a time through a 5-deep LDS ring per
 // operand (global_load_lds_dwordx4 straight from global memory; a slot is
 // 256 rows of 64 bytes, 16 KB; the two rings fill the 160 KB of LDS), so the
-// copies of a step are issued four steps (about 4 K cycles) before it runs:
-// with one wave per SIMD nothing else hides the memory latency.  16-byte
-// chunks are XOR-swizzled by (row >> 2) & 3 so that the operand reads (one
-// 16-byte chunk per lane, 32 rows by 2 chunks per wave) meet no bank
-// conflicts.  A step runs 2 k-substeps of 16 matrix ops with the copies of
-// step + 4 spread among the second; one barrier per step, between them.
+// copies of a step are issued four steps ahead: with one wave per SIMD
+// nothing else hides the memory latency.  16-byte chunks are XOR-swizzled by
+// (row >> 2) & 3 so that the operand reads (one 16-byte chunk per lane, 16
+// rows by 4 chunks per instruction) meet no bank conflicts.  A step is 64
+// matrix ops in two halves with one barrier between them; each half issues
+// 4 of the 8 copies of step + 4, and the second half reads all of step + 1's
+// operands, so a step's ops never wait on LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -45,8 +54,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kTileM = 256;
@@ -55,7 +64,6 @@ constexpr int kTileK = 32;                    // K per ring slot
 constexpr int kRowBytes = kTileK * 2;         // 64 bytes per operand row in LDS
 constexpr int kSlotBytes = 256 * kRowBytes;   // 16 KB per operand per slot
 constexpr int kStages = 5;                    // ring depth
-constexpr int kSubsteps = kTileK / 16;        // matrix-op k-steps per slot
 constexpr int kCopies = 8;                    // 1 KB copies per wave per step
 constexpr int kThreads = 256;
 
@@ -80,6 +88,12 @@ __device__ __forceinline__ void copy_1k(uint32_t lds_dst, const void* gbase, uin
       : "memory", "m0");
 }
 
+// One 16x16x32 bf16 matrix op into an accumulator held in AGPRs.  As inline
+// assembly the accumulator cannot be moved between registers around it.
+__device__ __forceinline__ void mfma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 __device__ __forceinline__ const void* uniform(const void* p) {
   const uint64_t u = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
@@ -87,13 +101,14 @@ __device__ __forceinline__ const void* uniform(const void* p) {
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Waits until at most 24 (16) of this wave's copies are in flight.
+// Waits until at most 24 (20) of this wave's copies are in flight.
 __device__ __forceinline__ void wait_copies_24() { __builtin_amdgcn_s_waitcnt(0x4F78); }
-__device__ __forceinline__ void wait_copies_16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+__device__ __forceinline__ void wait_copies_20() { __builtin_amdgcn_s_waitcnt(0x4F74); }
 
 // Workgroup barrier; the wave's own LDS reads are complete before it arrives.
 __device__ __forceinline__ void barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), seen by the compiler's wait tracking
+  __builtin_amdgcn_s_barrier();
 }
 
 template <typename TOut>
@@ -150,38 +165,26 @@ void gemm_bf16_kernel(GemmParams p) {
               uniform(wbase + (int64_t)ks * kTileK), w_off[n - 4]);
   };
 
-  // Operand reads: block b of this wave, k-substep kk: row 32 b + lane % 32
-  // of the wave's 128 rows, logical chunk 2 kk + lane / 32.
+  // Operand reads (16x16x32 ops): block b of this wave, row 16 b + lane % 16
+  // of the wave's 128 rows, logical chunk lane / 16 (the whole 32-deep step).
   const int wm = wave >> 1, wn = wave & 1;
-  int rd_off[4][kSubsteps];  // [block][kk] byte offset within a slot (A and W alike)
+  int rd_off[8];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int kk = 0; kk < kSubsteps; ++kk) {
-      const int r = 32 * b + (lane & 31);
-      rd_off[b][kk] = r * kRowBytes + swz(r, 2 * kk + (lane >> 5)) * 16;
-    }
+  for (int b = 0; b < 8; ++b) {
+    const int r = 16 * b + (lane & 15);
+    rd_off[b] = r * kRowBytes + swz(r, lane >> 4) * 16;
+  }
   const char* a_rd = &lds_a[0][0] + wm * 128 * kRowBytes;
   const char* w_rd = &lds_w[0][0] + wn * 128 * kRowBytes;
 
-  f32x16 acc[4][4];  // [a block (C rows)][w block (C columns)], each C^T
+  f32x4 acc[8][8];  // [a block (C rows)][w block (C columns)], each C^T
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = (f32x16){};
+    for (int jj = 0; jj < 8; ++jj) acc[i][jj] = (f32x4){};
 
-  // K loop.  Step ks sits in slot ks % 5 and runs 2 k-substeps of 16 matrix
-  // ops.  The barrier sits between them: once this wave's copies of step
-  // ks + 1 are in (the two later steps' copies may still fly), a barrier
-  // makes everyone's visible and frees the slot of step ks - 1 (every wave is
-  // past its reads).  After it the wave issues the copies of step ks + 4
-  // into that slot, one after every 2 ops of the second substep, and reads
-  // step ks + 1's first operands, so that the next step starts on operands
-  // already in registers.  Operands are read one substep ahead throughout.
-  // Past the last step the copies repeat it into slots nothing reads, so
-  // every step issues the same copies and the wait counts stay constant.
   const int nk = (int)(p.k / kTileK);
-  bf16x8 av[2][4], wv[2][4];
+  bf16x8 av[2][8], wv[2][8];
   if (nk > 0) {
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
@@ -190,83 +193,115 @@ void gemm_bf16_kernel(GemmParams p) {
     wait_copies_24();
     barrier();
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      av[0][b] = *(const bf16x8*)(a_rd + rd_off[b][0]);
-      wv[0][b] = *(const bf16x8*)(w_rd + rd_off[b][0]);
+    for (int b = 0; b < 8; ++b) {
+      av[0][b] = *(const bf16x8*)(a_rd + rd_off[b]);
+      wv[0][b] = *(const bf16x8*)(w_rd + rd_off[b]);
     }
   }
+  // K loop.  Step ks sits in slot ks % 5; its operands are already in
+  // registers (buffer ks & 1), read during step ks - 1.  Slot ks - 1 was last
+  // read before the previous barrier, so both halves of step ks refill it
+  // with the copies of step ks + 4.  At the barrier this wave's copies of
+  // step ks + 1 have landed (at most the later steps' 8 + 8 and this step's
+  // first 4 are in flight); the barrier makes everyone's visible, and the
+  // second half reads them.  Past the last step the copies repeat it into
+  // slots nothing reads, so every step issues the same copies and the wait
+  // counts stay constant.  K is a multiple of 64: steps come in pairs.
   int slot = 0;
-  for (int ks = 0; ks < nk; ++ks) {
+  auto step = [&](int ks, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr int nxt = cur ^ 1;
     const int fill = slot == 0 ? kStages - 1 : slot - 1;
     const int next = slot == kStages - 1 ? 0 : slot + 1;
     const int ks_fill = min(ks + kStages - 1, nk - 1);
-    const char* ab = a_rd + slot * kSlotBytes;
-    const char* wb = w_rd + slot * kSlotBytes;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      av[1][b] = *(const bf16x8*)(ab + rd_off[b][1]);
-      wv[1][b] = *(const bf16x8*)(wb + rd_off[b][1]);
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int q = 0; q < 4; ++q) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        acc[q4][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[0][jj], av[0][q4],
-                                                              acc[q4][jj], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    wait_copies_16();
-    barrier();
-    if (ks + 1 < nk) {
-      const char* an = a_rd + next * kSlotBytes;
-      const char* wn = w_rd + next * kSlotBytes;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        av[0][b] = *(const bf16x8*)(an + rd_off[b][0]);
-        wv[0][b] = *(const bf16x8*)(wn + rd_off[b][0]);
+      for (int jj = 0; jj < 8; ++jj) {
+        mfma16(acc[q][jj], wv[cur][jj], av[cur][q]);
+        if (jj == 4) copy_n(ks_fill, fill, q);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_copies_20();
+    barrier();
+    const char* an = a_rd + next * kSlotBytes;
+    const char* wn_ = w_rd + next * kSlotBytes;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int q = 4; q < 8; ++q) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        acc[q4][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[1][jj], av[1][q4],
-                                                              acc[q4][jj], 0, 0, 0);
-        if (jj & 1) copy_n(ks_fill, fill, 2 * q4 + (jj >> 1));
+      for (int jj = 0; jj < 8; ++jj) {
+        mfma16(acc[q][jj], wv[cur][jj], av[cur][q]);
+        // The next step's W operands first (its first ops need all of them),
+        // then its A operands in the order its ops use them.
+        if (jj % 2 == 1) {
+          const int r = 4 * (q - 4) + jj / 2;  // 0..15 over the half
+          if (r < 8)
+            wv[nxt][r] = *(const bf16x8*)(wn_ + rd_off[r]);
+          else
+            av[nxt][r - 8] = *(const bf16x8*)(an + rd_off[r - 8]);
+        }
+        if (jj == 4) copy_n(ks_fill, fill, q);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     slot = next;
+  };
+  for (int ks = 0; ks < nk; ks += 2) {
+    step(ks, std::integral_constant<int, 0>{});
+    step(ks + 1, std::integral_constant<int, 1>{});
   }
   // The repeated copies of the last steps land before the workgroup's LDS
   // can be handed to another workgroup.
   __builtin_amdgcn_s_waitcnt(0xF70);
+  // The last matrix ops' results settle before vector code reads them (the
+  // compiler does not see the latency of the assembly ops).
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) asm volatile("" : "+a"(acc[i][jj]));
 
-  // Epilogue: C[row][col .. col + 3] from registers 4 g .. 4 g + 3 of block
-  // (i, jj): row = 128 wm + 32 i + lane % 32, col = 128 wn + 32 jj + 8 g +
-  // 4 (lane / 32).  N is a multiple of 8, so a 4-column piece is all in or
-  // all out.
+  // Epilogue.  Block (i, jj) holds C rows 128 wm + 16 i + lane % 16 and
+  // columns 128 wn + 16 jj + 4 (lane / 16) .. + 3 in its 4 registers.
+  if constexpr (sizeof(TOut) == 2) {
+    // bf16 C goes through LDS (the ring is idle: every copy has landed and,
+    // after the barrier, every wave is past its operand reads) and leaves as
+    // 16-byte pieces of whole rows: 4 rows of 256 bytes per store.  Each
+    // wave stages its 128 x 128 quarter in its own area, rows padded to 272
+    // bytes (conflict-free for both the 8-byte writes and 16-byte reads).
+    barrier();
+    constexpr int kStageRow = 272;
+    char* stage = (wave < 2 ? &lds_a[0][0] : &lds_w[0][0]) + (wave & 1) * (128 * kStageRow);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 128 * wm + 32 * i + (lane & 31);
-    if (r >= rows) continue;
-    TOut* crow = (TOut*)p.c + (row0 + r) * p.ldc + col0;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < 8; ++jj) {
+        const f32x4 v = acc[i][jj];
+        const bf16x4 x = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *(bf16x4*)(stage + (16 * i + (lane & 15)) * kStageRow + (16 * jj + 4 * (lane >> 4)) * 2) = x;
+      }
+    const int cc = 128 * wn + 8 * (lane & 15);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cc = 128 * wn + 32 * jj + 8 * g + 4 * (lane >> 5);
+    for (int s4 = 0; s4 < 32; ++s4) {
+      const int r = 4 * s4 + (lane >> 4);
+      const u32x4 x = *(const u32x4*)(stage + r * kStageRow + (lane & 15) * 16);
+      if (128 * wm + r < rows && cc < cols)
+        *(u32x4*)((TOut*)p.c + (row0 + 128 * wm + r) * p.ldc + col0 + cc) = x;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 128 * wm + 16 * i + (lane & 15);
+      if (r >= rows) continue;
+      TOut* crow = (TOut*)p.c + (row0 + r) * p.ldc + col0;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int cc = 128 * wn + 16 * jj + 4 * (lane >> 4);
         if (cc >= cols) continue;
-        const f32x4 v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
-                         acc[i][jj][4 * g + 3]};
-        if constexpr (sizeof(TOut) == 2) {
-          const bf16x4 x = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *(bf16x4*)(crow + cc) = x;
-        } else {
-          *(f32x4*)(crow + cc) = v;
-        }
+        *(f32x4*)(crow + cc) = acc[i][jj];
       }
     }
   }
