@@ -37,7 +37,9 @@
  *    accumulators overflow at 2^128); beyond that an output may become inf
  *    where the exact result is finite.  The fp32 path keeps a true running
  *    max and has no such limit.
- *  - Calls are stateless and thread-safe.
+ *  - Calls are thread-safe.  The only state kept between calls is a cache of
+ *    each device's compute-unit count, filled on first use with atomic
+ *    stores of the same value.
  */
 #ifndef SHATTN_H
 #define SHATTN_H
