@@ -123,19 +123,21 @@ def test_m0_checker_flags_a_compiler_write():
     assert _m0_writers_outside_asm(ok) == []
 
 
-def test_built_bf16_kernel_leaves_m0_to_its_copies(tmp_path):
+@pytest.mark.parametrize("source", ["attn_fwd_bf16.hip", "gemm_bf16.hip"])
+def test_built_kernels_leave_m0_to_their_copies(source, tmp_path):
     """The global->LDS copies take their LDS address from M0, written by the
-    kernel's own assembly one or more instructions earlier (in the hot loop,
-    a schedule step earlier).  The compiler treats M0 as reserved and may not
-    honour an asm clobber of it, so the build must show that the compiler
-    itself never writes M0 and emits no M0-reading copy of its own."""
+    kernel's own assembly (in the attention kernel's hot loop, a schedule
+    step earlier; in the GEMM, in the copy's own block).  The compiler treats
+    M0 as reserved and may not honour an asm clobber of it, so the build must
+    show that the compiler itself never writes M0 and emits no M0-reading
+    copy of its own."""
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     flags = [f for f in libbuild.HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
-    out = tmp_path / "bf16.s"
+    out = tmp_path / (source + ".s")
     cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(libbuild.ROOT, "include"),
-           "-o", str(out), os.path.join(libbuild.CSRC, "attn_fwd_bf16.hip")]
+           "-o", str(out), os.path.join(libbuild.CSRC, source)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     text = out.read_text()
