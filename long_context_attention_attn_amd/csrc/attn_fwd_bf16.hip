@@ -23,10 +23,10 @@
 //   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]   4 d blocks x 4 steps
 //     A = V^T, read from row-major V in LDS with the transposing
 //         ds_read_b64_tr_b16, B = P^T taken straight from the S^T accumulator.
-// A K operand read from LDS feeds both query blocks in key block 0 and one
-// of them in key block 1 (read twice there), a V operand feeds both: LDS
-// traffic per flop is well below that of 32-row waves, which is what bounds
-// the matrix cores when they are fed from LDS.
+// In the main walk a K operand read from LDS feeds both query blocks, and so
+// does a V operand (the masked tiles run one query block at a time and read
+// them once per block): LDS traffic per flop is well below that of 32-row
+// waves, which is what bounds the matrix cores when they are fed from LDS.
 // Each lane owns one query column of S^T per query block, so the softmax
 // row max/sum are in-lane reductions plus one v_permlane32_swap with the
 // lane holding the other half of the keys.  Accumulator layout (lane l,
