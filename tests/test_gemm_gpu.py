@@ -55,6 +55,9 @@ def _run(a, w, nch, rank):
     (96, 8, 64, 3, 2),           # tiny chunks, one 8-column piece
     (4 * 300, 520, 192, 4, 3),   # ragged row tiles per chunk, 3 column tiles
     (2048, 1024, 512, 8, 5),     # more row tiles than XCDs
+    # 8 or more column tiles: the XCDs split the columns in two halves.
+    (3 * 700, 9 * 256 - 8, 128, 3, 2),   # 9 column tiles (halves of 5 and 4), ragged
+    (4 * 512, 8 * 256, 64, 4, 0),        # exactly 8 column tiles, full row tiles
 ])
 def test_small_shapes_full(m, n, k, nch, rank):
     a, w = gen_gemm(m=m, n=n, k=k, num_chunks=nch, device=DEV, seed=m + n + k)
