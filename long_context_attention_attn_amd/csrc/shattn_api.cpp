@@ -75,7 +75,10 @@ int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v
   // one workgroup per item).
   const int64_t bm = shattn::block_m((DType)d->in_dtype);
   const int64_t tiles = (d->seq_q + bm - 1) / bm;
-  if (tiles * (int64_t)d->batch * d->heads_q > INT32_MAX) return SHATTN_EUNSUPPORTED;
+  // Each factor is bounded first, so that no product overflows.
+  const int64_t heads = (int64_t)d->batch * d->heads_q;  // < 2^62
+  if (tiles > INT32_MAX || heads > INT32_MAX || tiles * heads > INT32_MAX)
+    return SHATTN_EUNSUPPORTED;
   return SHATTN_OK;
 }
 
@@ -352,8 +355,13 @@ int allgather_gemm_shifted(const shattn_gemm_desc* desc, const void* a, const vo
   const int64_t tiles_per_chunk = (chunk_rows + 255) / 256;
   const int64_t tiles_m = tiles_per_chunk * num_chunks;
   const int64_t tiles_n = (d.n + 255) / 256;
-  if (tiles_m > INT32_MAX / 8 || ((tiles_m + 7) / 8) * 8 * tiles_n > INT32_MAX)
-    return SHATTN_EUNSUPPORTED;
+  // The launch's grid is one of two shapes (the XCDs all on every column
+  // tile, or split into row groups and column halves); each factor is
+  // bounded first, so that no product overflows.
+  if (tiles_m > INT32_MAX / 8 || tiles_n > INT32_MAX) return SHATTN_EUNSUPPORTED;
+  const int64_t grid_all_columns = ((tiles_m + 7) / 8) * 8 * tiles_n;
+  const int64_t grid_split = 8 * ((tiles_m + 3) / 4) * ((tiles_n + 1) / 2);
+  if (grid_all_columns > INT32_MAX || grid_split > INT32_MAX) return SHATTN_EUNSUPPORTED;
   if (empty) return SHATTN_OK;
   shattn::GemmParams p = {};
   p.a = a;

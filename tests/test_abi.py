@@ -127,6 +127,10 @@ def test_shifted_rejects_bad_arguments():
     assert _shifted(lib, d, lse=FAKE + 2) == 1
     # KV rows are indexed in 32-bit arithmetic: more than 2^31 - 64 is refused.
     assert _shifted(lib, d, total=(1 << 31) - 56, nch=8) == 2
+    # Work items beyond 2^31 are refused without overflowing the count
+    # (2^52 query tiles times 2^61 (batch, head) pairs).
+    big = _desc(batch=(1 << 31) - 1, heads_q=1 << 30, heads_kv=1 << 30, seq_q=1 << 60)
+    assert _shifted(lib, big) == 2
 
 
 def test_chunk_accumulate_rejects_bad_arguments():
@@ -271,6 +275,11 @@ def test_gemm_rejects_bad_arguments():
     assert _gemm(lib, d, c=FAKE + 8) == 1
     # fp32 C: a row stride of 260 floats (1040 bytes) is 16-byte aligned.
     assert _gemm(lib, _gdesc(out_dtype=binding.F32, ldc=260, n=256), a=0, nch=4) == 1
+    # A grid beyond 2^31 workgroups is refused without overflowing the count
+    # (2^28 row tiles times 2^52 column tiles).
+    assert _gemm(lib, _gdesc(m=1 << 36, n=1 << 60, k=64, lda=64, ldw=64, ldc=1 << 60)) == 2
+    # K == 0 writes zeros: A and W are never read and may be null.
+    assert _gemm(lib, _gdesc(k=0, lda=0, ldw=0), a=0, w=0, c=0) == 1   # C is still needed
     # Nothing to compute: a no-op that touches no pointer.
     assert _gemm(lib, _gdesc(m=0), a=0, w=0, c=0) == 0
     assert _gemm(lib, _gdesc(n=0, ldc=0), a=0, w=0, c=0) == 0
