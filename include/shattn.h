@@ -21,7 +21,10 @@
  *    never synchronize; outputs are valid once the stream reaches that
  *    point.
  *  - Every argument is validated on the host before anything is launched; on
- *    failure the call returns a non-zero status and launches nothing.  No
+ *    failure the call returns a non-zero status and launches nothing.  Among
+ *    the checks: the last element of every tensor, from its sizes and
+ *    strides, must lie within 2^60 elements of its base pointer (kernels
+ *    address elements in 64-bit arithmetic), else SHATTN_EINVAL.  No
  *    exceptions cross this boundary and nothing aborts.
  *  - NaN/Inf in inputs propagate to the outputs; they are never masked.  In
  *    the bf16 path they can also reach a few rows that do not see them:

@@ -43,6 +43,15 @@ bool strides_ok(const int64_t s[3], int64_t esize) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? SHATTN_OK : SHATTN_EHIP; }
 
+// The element offset of the last element of a [n0, n1, n2, inner] tensor with
+// strides s (a non-empty one), computed without overflow, must stay within
+// kPosLimit: the kernels address elements in 64-bit arithmetic.
+bool extent_ok(const int64_t s[3], int64_t n0, int64_t n1, int64_t n2, int64_t inner) {
+  const __int128 last = (__int128)(n0 - 1) * s[0] + (__int128)(n1 - 1) * s[1] +
+                        (__int128)(n2 - 1) * s[2] + inner;
+  return last <= kPosLimit;
+}
+
 // Checks shared by attn_chunk_fwd and attn_shifted_fwd.  `o_esize` is the
 // element size of the O tensor of the call.
 int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v, const void* o,
@@ -66,6 +75,12 @@ int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v
     return SHATTN_EUNSUPPORTED;
   const bool q_empty = d->batch == 0 || d->seq_q == 0;
   const bool kv_empty = d->batch == 0 || kv_rows == 0;
+  if (!q_empty && (!extent_ok(d->q_stride, d->batch, d->heads_q, d->seq_q, d->head_dim) ||
+                   !extent_ok(d->o_stride, d->batch, d->heads_q, d->seq_q, d->head_dim)))
+    return SHATTN_EINVAL;
+  if (!kv_empty && (!extent_ok(d->k_stride, d->batch, d->heads_kv, kv_rows, d->head_dim) ||
+                    !extent_ok(d->v_stride, d->batch, d->heads_kv, kv_rows, d->head_dim)))
+    return SHATTN_EINVAL;
   if (!q_empty && (q == nullptr || o == nullptr || lse == nullptr)) return SHATTN_EINVAL;
   if (!kv_empty && (k == nullptr || v == nullptr)) return SHATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SHATTN_EINVAL;
@@ -346,6 +361,12 @@ int allgather_gemm_shifted(const shattn_gemm_desc* desc, const void* a, const vo
   if (!empty && (a == nullptr && d.k > 0)) return SHATTN_EINVAL;
   if (!empty && ((w == nullptr && d.k > 0) || c == nullptr)) return SHATTN_EINVAL;
   if (d.lda < d.k || d.ldw < d.k || d.ldc < d.n) return SHATTN_EINVAL;
+  if (!empty) {  // the last element of A, W and C within 64-bit element offsets
+    const int64_t ra[3] = {0, 0, d.lda}, rw[3] = {0, 0, d.ldw}, rc[3] = {0, 0, d.ldc};
+    if (!extent_ok(ra, 1, 1, d.m, d.k) || !extent_ok(rw, 1, 1, d.n, d.k) ||
+        !extent_ok(rc, 1, 1, d.m, d.n))
+      return SHATTN_EINVAL;
+  }
   if (d.lda % 8 != 0 || d.ldw % 8 != 0 || d.ldc % (d.out_dtype == SHATTN_F32 ? 4 : 8) != 0)
     return SHATTN_EINVAL;
   if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return SHATTN_EINVAL;

@@ -128,9 +128,17 @@ def test_shifted_rejects_bad_arguments():
     # KV rows are indexed in 32-bit arithmetic: more than 2^31 - 64 is refused.
     assert _shifted(lib, d, total=(1 << 31) - 56, nch=8) == 2
     # Work items beyond 2^31 are refused without overflowing the count
-    # (2^52 query tiles times 2^61 (batch, head) pairs).
-    big = _desc(batch=(1 << 31) - 1, heads_q=1 << 30, heads_kv=1 << 30, seq_q=1 << 60)
+    # (2^44 query tiles times 2^61 (batch, head) pairs; zero batch and head
+    # strides keep every tensor's extent in range).
+    flat = S3(0, 0, 128)
+    big = _desc(batch=(1 << 31) - 1, heads_q=1 << 30, heads_kv=1 << 30, seq_q=1 << 52,
+                q_stride=flat, k_stride=flat, v_stride=flat, o_stride=flat)
     assert _shifted(lib, big) == 2
+    # Strides whose last element lies beyond 2^60 elements (64-bit offsets in
+    # the kernels would wrap) are refused.
+    far = _desc(batch=1 << 20, k_stride=S3(1 << 50, 1 << 20, 128))
+    assert _shifted(lib, far) == 1
+    assert _shifted(lib, _desc(batch=1 << 20, o_stride=S3(1 << 50, 1 << 20, 128))) == 1
 
 
 def test_chunk_accumulate_rejects_bad_arguments():
@@ -275,9 +283,11 @@ def test_gemm_rejects_bad_arguments():
     assert _gemm(lib, d, c=FAKE + 8) == 1
     # fp32 C: a row stride of 260 floats (1040 bytes) is 16-byte aligned.
     assert _gemm(lib, _gdesc(out_dtype=binding.F32, ldc=260, n=256), a=0, nch=4) == 1
-    # A grid beyond 2^31 workgroups is refused without overflowing the count
-    # (2^28 row tiles times 2^52 column tiles).
-    assert _gemm(lib, _gdesc(m=1 << 36, n=1 << 60, k=64, lda=64, ldw=64, ldc=1 << 60)) == 2
+    # A grid beyond 2^31 workgroups (2^22 x 2^22 tiles; every extent within
+    # 2^60 elements) is refused.
+    assert _gemm(lib, _gdesc(m=1 << 30, n=1 << 30, k=64, lda=64, ldw=64, ldc=1 << 30)) == 2
+    # Rows whose last element lies beyond 2^60 elements are refused.
+    assert _gemm(lib, _gdesc(m=1 << 40, lda=1 << 21, ldw=512)) == 1
     # K == 0 writes zeros: A and W are never read and may be null.
     assert _gemm(lib, _gdesc(k=0, lda=0, ldw=0), a=0, w=0, c=0) == 1   # C is still needed
     # Nothing to compute: a no-op that touches no pointer.
