@@ -239,6 +239,10 @@ GEMM_WORKLOADS = (
                  summary="Llama-3-8B-like MLP gate+up projection, tensor parallel over 8 "
                          "GPUs: batch 16 x 2048 tokens gathered from 8 row chunks, the "
                          "rank's 3584-column weight shard (2 x 14336 / 8), rank 3"),
+    GemmWorkload(102, "llama3_8b_tp8_qkv_b16", 32768, 768, 4096, 8, 5,
+                 summary="Llama-3-8B-like attention QKV projection, tensor parallel over "
+                         "8 GPUs: the same gathered activation, the rank's 768-column "
+                         "weight shard ((4096 + 2 x 1024) / 8), rank 5"),
 )
 
 GEMM_BY_NAME = {w.name: w for w in GEMM_WORKLOADS}

@@ -100,7 +100,8 @@ def test_zero_k_writes_zeros():
     assert bool((c == 0).all())
 
 
-@pytest.mark.parametrize("name", ["gemm_tiny_ragged", "llama3_8b_tp8_mlp_b16"])
+@pytest.mark.parametrize("name", ["gemm_tiny_ragged", "llama3_8b_tp8_mlp_b16",
+                                  "llama3_8b_tp8_qkv_b16"])
 def test_workload_every_element(name):
     """Each GEMM workload at its full size, in the benchmark's launch
     configuration, every element against the oracle."""
