@@ -73,3 +73,28 @@ def test_heavy_rows():
     heavy = (ratio - 8.0).abs().amax(dim=1) < 1e-6
     plain = (ratio - 1.0).abs().amax(dim=1) < 1e-6
     assert int(heavy.sum()) == 10 and bool((heavy | plain).all())
+
+
+def test_gemm_table_and_generator():
+    from long_context_attention_attn_amd.workloads import GEMM_BY_NAME, GEMM_WORKLOADS, gen_gemm
+
+    for w in GEMM_WORKLOADS:
+        assert w.m % w.num_chunks == 0 and 0 <= w.rank < w.num_chunks
+        assert w.k % 64 == 0 and w.n % 8 == 0  # what the kernel supports
+        assert sorted(w.visit_order()) == list(range(w.num_chunks))
+        assert w.visit_order()[0] == w.rank
+        assert w.flops() == 2 * w.m * w.n * w.k
+    big = GEMM_BY_NAME["llama3_8b_tp8_mlp_b16"]
+    assert (big.m, big.n, big.k, big.num_chunks) == (16 * 2048, 2 * 14336 // 8, 4096, 8)
+    qkv = GEMM_BY_NAME["llama3_8b_tp8_qkv_b16"]
+    assert qkv.n == (4096 + 2 * 1024) // 8
+    # Deterministic; each row chunk of A comes from its own generator, so one
+    # chunk can be regenerated alone; W is scaled by 1/sqrt(K).
+    a1, w1 = gen_gemm(m=12, n=8, k=64, num_chunks=3, seed=5)
+    a2, w2 = gen_gemm(m=12, n=8, k=64, num_chunks=3, seed=5)
+    assert torch.equal(a1, a2) and torch.equal(w1, w2)
+    g = torch.Generator().manual_seed(slice_seed(5, 0, 0, 1))
+    assert torch.equal(a1[4:8], torch.randn((4, 64), generator=g).to(torch.bfloat16))
+    g = torch.Generator().manual_seed(slice_seed(5, 1, 0, 0))
+    assert torch.equal(w1, (torch.randn((8, 64), generator=g) / 8.0).to(torch.bfloat16))
+    assert a1.dtype == torch.bfloat16 and w1.shape == (8, 64)
