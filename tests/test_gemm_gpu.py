@@ -80,15 +80,23 @@ def test_every_rank_same_result():
     _check(outs[0], outs[0].to(torch.bfloat16), a, w)
 
 
-def test_strided_operands():
-    """Row strides above K and N (views into wider buffers)."""
-    m, n, k, nch = 600, 264, 128, 2
+@pytest.mark.parametrize("m,n,nch", [(600, 264, 2), (3 * 520, 9 * 256 - 16, 3)])
+def test_strided_operands(m, n, nch):
+    """Row strides above K and N (views into wider buffers), fp32 and bf16 C
+    (the bf16 C leaves through the LDS-staged epilogue; the second shape
+    takes the split-column path)."""
+    k = 128
     a_big, w_big = gen_gemm(m=m, n=n, k=k + 64, num_chunks=nch, device=DEV, seed=11)
     a, w = a_big[:, 32:32 + k], w_big[:, 64:64 + k]
-    out_big = torch.empty((m, n + 40), dtype=torch.float32, device=DEV)
-    c32 = binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=1, out=out_big[:, :n])
+    out32 = torch.full((m, n + 40), 7.0, dtype=torch.float32, device=DEV)
+    out16 = torch.full((m, n + 40), 7.0, dtype=torch.bfloat16, device=DEV)
+    c32 = binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=1, out=out32[:, :n])
+    c16 = binding.allgather_gemm_shifted(a, w, num_chunks=nch, rank=1, out=out16[:, :n])
     torch.cuda.synchronize()
-    _check(c32, c32.to(torch.bfloat16), a, w)
+    assert torch.equal(c32.to(torch.bfloat16), c16)
+    _check(c32, c16, a, w)
+    # The columns past N of each row are left alone.
+    assert bool((out32[:, n:] == 7.0).all()) and bool((out16[:, n:] == 7.0).all())
 
 
 def test_zero_k_writes_zeros():
