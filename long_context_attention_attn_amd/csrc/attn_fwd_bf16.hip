@@ -1,7 +1,11 @@
 // Fused shifted-chunk attention forward, bf16 inputs, for gfx950 (CDNA4).
 //
-// A work item is 256 query rows of one (batch, query head): four waves, one
-// per SIMD, of 64 rows each (two 32-row query blocks).  The grid has at most
+// A work item is four waves, one per SIMD, of 64 query rows each (two
+// 32-row query blocks): 256 rows of one (batch, query head), or, when each KV
+// head serves a multiple of 4 query heads, the same 64 rows of 4 query heads
+// that share one KV head (the waves then share their causal limits, so an
+// item's diagonal band is one or two 64-key tiles, not four, and no wave
+// computes tiles none of its queries sees).  The grid has at most
 // one workgroup per CU, each working through a fixed list of items (see the
 // block -> item mapping in the kernel): the hardware hands out waiting
 // workgroups in bursts to whichever CUs are free, which pairs heavy causal
@@ -474,7 +478,11 @@ __device__ __forceinline__ void settle(const T& v) {
   asm volatile("" ::"v"(v));
 }
 
-template <typename TOut>
+// kQuad: an item is 64 query rows of 4 query heads of one KV head's group (wave
+// w takes head 4 g + w), else 256 rows of one head (wave w takes rows
+// 64 w .. 64 w + 63).  A compile-time choice: chosen at run time, the
+// register allocator spilled per-lane constants to scratch.
+template <typename TOut, bool kQuad>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_bf16_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[kRing][kTile];
@@ -493,7 +501,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const int lq = lane & 31;
   const int hh = lane >> 5;
 
-  // Blocks -> work items (b, kv head, query head of its group, query tile).
+  // Blocks -> work items (b, kv head, query head of its group or group of 4
+  // of them, query tile).
   // The grid holds at most one block per CU; each block walks a list of
   // items.  The hardware deals consecutive blocks round-robin to the 8 XCDs:
   // when the KV heads split evenly, the blocks of XCD x share the items of
@@ -504,7 +513,8 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   const int n_blocks = (int)gridDim.x;
   const int bid = (int)blockIdx.x;
   const int nkv = p.batch * p.heads_kv;
-  const int per_head = p.group * p.num_q_tiles;
+  const int per_tile = kQuad ? p.group >> 2 : p.group;  // items per query tile and KV head
+  const int per_head = per_tile * p.num_q_tiles;
   const bool by_xcd = (nkv & 7) == 0 && (n_blocks & 7) == 0;
   const int lanes = by_xcd ? (n_blocks >> 3) : n_blocks;
   const int lidx = by_xcd ? (bid >> 3) : bid;
@@ -515,17 +525,18 @@ void attn_fwd_bf16_kernel(FwdParams p) {
   if (item >= n_list) break;
   const int kvi = (by_xcd ? xcd + 8 * (item / per_head) : item / per_head);
   const int i_in = item % per_head;
-  const int qt = p.num_q_tiles - 1 - i_in / p.group;
-  const int g = i_in % p.group;
+  const int qt = p.num_q_tiles - 1 - i_in / per_tile;
+  const int g = i_in % per_tile;
   const int hk = kvi % p.heads_kv;
   const int b = kvi / p.heads_kv;
-  const int h = hk * p.group + g;
+  const int h = hk * p.group + (kQuad ? 4 * g + wave : g);  // this wave's query head
   // Every wave is done with the previous item's LDS tiles.
   if (round > 0) __syncthreads();
 
-  const int64_t q_start = (int64_t)qt * kBlockM;
-  const int64_t q_rows_wg = min((int64_t)kBlockM, p.seq_q - q_start);
-  const int64_t wave_q0 = q_start + wave * 64;
+  constexpr int rows_item = kQuad ? 64 : kBlockM;
+  const int64_t q_start = (int64_t)qt * rows_item;
+  const int64_t q_rows_wg = min((int64_t)rows_item, p.seq_q - q_start);
+  const int64_t wave_q0 = q_start + (kQuad ? 0 : wave * 64);
   // Query positions relative to key row 0, clamped to [-1, kv_rows]: -1 sees
   // no key, kv_rows sees every key.
   const int kv_rows = p.kv_rows;
@@ -1256,15 +1267,16 @@ int device_cus() {
 
 template <typename TOut>
 hipError_t launch_typed(const FwdParams& p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.num_q_tiles * p.batch * p.heads_q;
+  const int64_t items = (int64_t)p.num_q_tiles * p.batch * p.heads_q / (p.quad_heads ? 4 : 1);
   if (items == 0) return hipSuccess;
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
   const int64_t blocks = std::min<int64_t>(items, cus);
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel((const void*)&attn_fwd_bf16_kernel<TOut>, dim3((unsigned)blocks),
-                         dim3(kThreads), args, 0, stream);
+  const void* fn = p.quad_heads ? (const void*)&attn_fwd_bf16_kernel<TOut, true>
+                                : (const void*)&attn_fwd_bf16_kernel<TOut, false>;
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace

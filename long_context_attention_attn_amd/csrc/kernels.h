@@ -41,6 +41,9 @@ struct FwdParams {
   // running (O, LSE) pair, instead of overwriting them (lse_merge's
   // arithmetic, in the kernel's epilogue).
   int32_t accumulate;
+  // bf16 kernel: 1 if a work item is 64 query rows of 4 query heads that
+  // share a KV head (one head per wave), 0 if it is 256 rows of one head.
+  int32_t quad_heads;
 };
 
 // Weights and LSE of the merge of (O_a, L_a) with (O_b, L_b):
@@ -66,8 +69,19 @@ constexpr int kBlockMBf16 = 256;
 constexpr int kBlockMF32 = 128;
 inline int block_m(DType in) { return in == DType::BF16 ? kBlockMBf16 : kBlockMF32; }
 
+// The bf16 kernel's work items.  When every KV head serves a multiple of 4
+// query heads, an item is 64 query rows of 4 of them (one per wave): all four
+// waves then share their causal limits, so an item's diagonal band spans one
+// or two 64-key tiles instead of four, and no wave computes tiles none of its
+// queries sees.  Otherwise an item is 256 rows of one head, 64 per wave.
+inline bool quad_heads(DType in, int64_t group) { return in == DType::BF16 && group % 4 == 0; }
+// Query rows per work item, and query heads per work item.
+inline int item_rows(DType in, int64_t group) { return quad_heads(in, group) ? 64 : block_m(in); }
+inline int item_heads(DType in, int64_t group) { return quad_heads(in, group) ? 4 : 1; }
+
 // Launches the fused forward kernel on `stream`; returns the HIP launch status.
-// p.num_q_tiles must equal ceil(seq_q / block_m(in)).
+// p.num_q_tiles must equal ceil(seq_q / item_rows(in, group)), and
+// p.quad_heads quad_heads(in, group).
 hipError_t launch_attn_fwd(const FwdParams& p, DType in, DType out, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, DType out, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdParams& p, DType out, hipStream_t stream);

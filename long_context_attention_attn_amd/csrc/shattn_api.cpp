@@ -85,10 +85,11 @@ int check_desc(const shattn_desc* d, const void* q, const void* k, const void* v
   if (!kv_empty && (k == nullptr || v == nullptr)) return SHATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SHATTN_EINVAL;
   if (((uintptr_t)lse & 3u) != 0) return SHATTN_EINVAL;
-  // Work items: block_m query rows of each (batch, head) (the bf16 kernel
-  // walks them with at most one workgroup per CU, the fp32 kernel launches
-  // one workgroup per item).
-  const int64_t bm = shattn::block_m((DType)d->in_dtype);
+  // Work items: item_rows query rows of item_heads query heads (the bf16
+  // kernel walks them with at most one workgroup per CU, the fp32 kernel
+  // launches one workgroup per item).  The count is bounded by tiles x heads.
+  const int64_t bm =
+      shattn::item_rows((DType)d->in_dtype, (int64_t)d->heads_q / d->heads_kv);
   const int64_t tiles = (d->seq_q + bm - 1) / bm;
   // Each factor is bounded first, so that no product overflows.
   const int64_t heads = (int64_t)d->batch * d->heads_q;  // < 2^62
@@ -126,8 +127,10 @@ FwdParams make_params(const shattn_desc* d, const void* q, const void* k, const 
   p.causal = d->causal;
   const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634074);
-  const int64_t bm = shattn::block_m((DType)d->in_dtype);
+  const DType in = (DType)d->in_dtype;
+  const int64_t bm = shattn::item_rows(in, p.group);
   p.num_q_tiles = (int32_t)((d->seq_q + bm - 1) / bm);
+  p.quad_heads = shattn::quad_heads(in, p.group) ? 1 : 0;
   return p;
 }
 

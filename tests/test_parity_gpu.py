@@ -722,3 +722,56 @@ def test_more_work_items_than_workgroups(hq, hkv, sq, causal):
                                                rows, causal=causal, q_pos0=q_pos0)
         assert _max_err(o[0, h].index_select(0, rows_t), o_ref) <= TOL_O[torch.bfloat16], h
         _check_lse(lse[0, h].index_select(0, rows_t), lse_ref)
+
+
+QUAD = [
+    # (B, Hq, Hkv, Sq, Skv, J, rank, causal, q_pos0, out): groups of 4 and 8 query heads
+    # per KV head, so the bf16 kernel's items are 64 query rows of 4 heads
+    (2, 8, 2, 333, 1536, 6, 5, True, 1100, torch.bfloat16),   # ragged rows, offset not 64-aligned
+    (1, 16, 2, 200, 1024, 4, 3, True, 700, torch.float32),    # two head quads per KV head
+    (1, 4, 1, 130, 512, 2, 1, False, 0, torch.bfloat16),      # non-causal, ragged last item
+    (1, 8, 1, 64, 960, 5, 2, True, 896, torch.float32),       # one item per quad, band at the end
+]
+
+
+@pytest.mark.parametrize("case", QUAD, ids=lambda c: "x".join(str(v) for v in c[:9]))
+def test_quad_head_items_full(case):
+    """Every element against the oracle for the work-item layout of 64 query
+    rows of 4 query heads sharing a KV head: the four waves of an item read
+    four different Q heads and share one causal limit."""
+    b, hq, hkv, sq, skv, nch, rank, causal, q_pos0, dout = case
+    _say(f"quad items {case}")
+    q, k, v = gen_qkv(batch=b, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=torch.bfloat16, device=DEV, seed=sq * 5 + hq)
+    o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=nch, rank=rank, causal=causal,
+                                      q_pos0=q_pos0, out_dtype=dout)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=causal, q_pos0=q_pos0)
+    assert _max_err(o, o_ref) <= TOL_O[torch.bfloat16]
+    _check_lse(lse, lse_ref)
+
+
+def test_quad_head_items_over_several_rounds():
+    """More 64-row, 4-head items than the one-per-CU grid has workgroups, with
+    a list per XCD (8 KV heads): 33 query tiles x 8 KV heads x 2 head quads =
+    528 items over 256 blocks.  The first and last row of every 64-row item of
+    every head are checked against the oracle, so every item and every wave
+    of it is."""
+    hq, hkv, sq, skv, nch, rank, q_pos0 = 64, 8, 2100, 4096, 4, 1, 1900
+    _say(f"quad items over rounds hq {hq} hkv {hkv} sq {sq}")
+    q, k, v = gen_qkv(batch=1, heads_q=hq, heads_kv=hkv, seq_q=sq, seq_kv=skv, head_dim=128,
+                      dtype=torch.bfloat16, device=DEV, seed=4242)
+    o, lse = binding.attn_shifted_fwd(q, k, v, num_chunks=nch, rank=rank, causal=True,
+                                      q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    rows = sorted(set(list(range(0, sq, 64)) + [min(t + 63, sq - 1) for t in range(0, sq, 64)]))
+    rows = np.array(rows, dtype=np.int64)
+    rows_t = torch.from_numpy(rows).to(o.device)
+    group = hq // hkv
+    for h in range(hq):
+        o_ref, lse_ref = oracle.attention_rows(q[0:1, h:h + 1].cpu(),
+                                               k[0:1, h // group:h // group + 1].cpu(),
+                                               v[0:1, h // group:h // group + 1].cpu(), 0, 0,
+                                               rows, causal=True, q_pos0=q_pos0)
+        assert _max_err(o[0, h].index_select(0, rows_t), o_ref) <= TOL_O[torch.bfloat16], h
+        _check_lse(lse[0, h].index_select(0, rows_t), lse_ref)
