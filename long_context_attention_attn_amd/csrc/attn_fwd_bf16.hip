@@ -104,7 +104,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kBlockMBf16;  // 256 query rows per workgroup
+constexpr int kBlockM = kBlockMBf16;  // query rows of a one-head work item (4 waves x 64)
 constexpr int kN = 64;                // keys per tile
 constexpr int kTile = kN * 128;       // elements of one K or V tile (16 KB, unpadded)
 constexpr int kTileBytes = kTile * 2;

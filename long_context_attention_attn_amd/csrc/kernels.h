@@ -64,7 +64,7 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
 
 enum class DType : int { BF16 = 0, F32 = 1 };
 
-// Query rows per workgroup of the forward kernels, per input type.
+// Query rows of a one-head work item of the forward kernels, per input type.
 constexpr int kBlockMBf16 = 256;
 constexpr int kBlockMF32 = 128;
 inline int block_m(DType in) { return in == DType::BF16 ? kBlockMBf16 : kBlockMF32; }
