@@ -210,6 +210,7 @@ def _composed(q, k, v, nch, rank, causal, q_pos0):
     (2, 4, 2, 200, 320, 5, 3, True, 120, torch.bfloat16),
     (1, 2, 2, 300, 300, 3, 0, True, 0, torch.bfloat16),
     (2, 2, 2, 100, 96, 3, 1, False, 0, torch.float32),
+    (1, 8, 2, 333, 1024, 4, 2, True, 500, torch.bfloat16),  # 4-head items, ragged rows
 ], ids=lambda c: "x".join(str(v) for v in c[:9]))
 def test_composed_chunk_merge_small_full(case):
     b, hq, hkv, sq, skv, nch, rank, causal, q_pos0, din = case
@@ -318,6 +319,7 @@ def _pinned_like(t, layout_bshd=False):
     (2, 4, 4, 130, 768, 3, 2, False, 0, torch.bfloat16, "host", True),
     (1, 2, 1, 200, 600, 5, 4, True, 400, torch.float32, "host", False),
     (1, 4, 2, 256, 512, 4, 1, True, 128, torch.bfloat16, "device", False),
+    (1, 8, 1, 300, 1024, 4, 1, True, 512, torch.bfloat16, "host", False),  # 4-head items, group 8
 ], ids=lambda c: "x".join(str(v) for v in c[:9]) + "-" + c[10] + ("-bshd" if c[11] else ""))
 def test_overlapped_chunk_walk(case):
     """Chunks copied in visit order on a second stream while earlier chunks
