@@ -77,8 +77,11 @@ typedef enum { SHATTN_BF16 = 0, SHATTN_F32 = 1 } shattn_dtype;
  * [batch, heads_kv, seq_kv, head_dim]; O is [batch, heads_q, seq_q, head_dim].
  * Strides are in ELEMENTS of the tensor's own dtype, for the (batch, head,
  * sequence) axes; the head_dim axis must be contiguous (stride 1).  A
- * sequence stride above 2^24 elements, or more than 2^31 - 64 key rows in one
- * call (kv_len, kv_len_total), is refused with SHATTN_EUNSUPPORTED.
+ * sequence stride above 2^24 elements, more than 2^31 - 64 key rows in one
+ * call (kv_len, kv_len_total), or ceil(seq_q / R) * batch * heads_q above
+ * 2^31 - 1 (R = 64 for bf16 inputs with heads_q / heads_kv a multiple of 4,
+ * 256 for other bf16 inputs, 128 for fp32) is refused with
+ * SHATTN_EUNSUPPORTED.
  *
  * Query head h reads KV head h / (heads_q / heads_kv) (contiguous GQA
  * groups; heads_q == heads_kv is MHA).

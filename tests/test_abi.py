@@ -134,6 +134,15 @@ def test_shifted_rejects_bad_arguments():
     big = _desc(batch=(1 << 31) - 1, heads_q=1 << 30, heads_kv=1 << 30, seq_q=1 << 52,
                 q_stride=flat, k_stride=flat, v_stride=flat, o_stride=flat)
     assert _shifted(lib, big) == 2
+    # With 4 query heads per KV head a bf16 work item is 64 query rows of 4
+    # heads, so the item count is bounded with 64-row tiles: 2^35 rows give
+    # 2^29 tiles x 4 heads = 2^31 items, one past the limit.  (The same rows
+    # in 256-row tiles would pass this check; such a call is not made here
+    # because it would be accepted and launched.)
+    quad = _desc(heads_q=4, heads_kv=1, seq_q=1 << 35,
+                 q_stride=flat, k_stride=flat, v_stride=flat, o_stride=flat)
+    assert _shifted(lib, quad) == 2
+    assert _chunk(lib, quad) == 2
     # Strides whose last element lies beyond 2^60 elements (64-bit offsets in
     # the kernels would wrap) are refused.
     far = _desc(batch=1 << 20, k_stride=S3(1 << 50, 1 << 20, 128))
