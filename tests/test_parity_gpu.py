@@ -733,6 +733,7 @@ QUAD = [
     (1, 16, 2, 200, 1024, 4, 3, True, 700, torch.float32),    # two head quads per KV head
     (1, 4, 1, 130, 512, 2, 1, False, 0, torch.bfloat16),      # non-causal, ragged last item
     (1, 8, 1, 64, 960, 5, 2, True, 896, torch.float32),       # one item per quad, band at the end
+    (2, 24, 2, 100, 512, 2, 1, True, 300, torch.bfloat16),    # three head quads per KV head
 ]
 
 
